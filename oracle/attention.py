@@ -1,0 +1,182 @@
+"""fp64 CPU oracle: exact scaled-dot-product attention written as its plain definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+What it computes, and where the pages fix it
+--------------------------------------------
+The memory-efficient method is exact: it reaches the same result as standard
+attention, only without storing the score matrix ("FlashAttention (2022):
+l'attenzione che non satura la memoria", section "L'idea: non scrivere mai la
+matrice intera"; the xFormers tutorial "Come costruire Transformer efficienti
+in memoria con xFormers...", section "Impostare xFormers e Validare
+l'Attenzione Memory-Efficient", which validates it against a standard
+implementation up to fp16 rounding). So this oracle is the plain definition,
+in float64, with the full score block of one (segment, head) held at once:
+
+  scores  = scale * q k^T                      (briefia.fr page "Transformer :
+                                                 comprendre l'entrainement et
+                                                 l'inference", class SelfAttention)
+  scores += ALiBi bias                          (xFormers tutorial, section
+                                                 "Utilizzare SwiGLU e ALiBi")
+  masked  -> -inf                               (causal: the same code's lower-
+                                                 triangular mask, shifted by the
+                                                 number of cached tokens)
+  p       = softmax over the allowed keys
+  o       = p v ;  lse = log sum exp(scores)
+
+Readings taken where the pages are silent (each also listed in the design doc):
+
+* scale is the caller's float32 value, widened exactly to float64;
+* causal alignment is bottom-right: query i of a segment with M queries and N
+  keys sees key j iff ``j <= i + (N - M)``. The KV-cache code of the
+  briefia.fr page builds its causal mask as a lower triangle shifted right by
+  the number of cached tokens, which is this rule; for M == N it is the usual
+  lower triangle;
+* ALiBi adds ``-slope[h] * |(i + N - M) - j|`` (segment-local positions,
+  query head ``h``, slope as the caller's float32) after scaling and before
+  masking; the pages name ALiBi but print no formula;
+* grouped-query attention maps query head ``h`` to KV head
+  ``h // (Hq // Hkv)``: the tutorial's GQA snippet lays q out as
+  ``[B, M, G, Hq/G, K]`` against k, v ``[B, M, G, 1, K]``, so consecutive
+  query heads share one KV head;
+* a query row with no allowed key returns o = 0 and lse = -inf;
+* decode: the newest token's k/v is already in the cache (briefia.fr page,
+  section "Pre-remplissage et decodage"); its query, at position ctx-1,
+  attends to cache rows 0..ctx-1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """uint16 bit patterns of fp16/bf16 -> exactly equal float64 values."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """KV head used by query head ``h`` (tutorial GQA snippet: q ``[.., G, Hq/G, K]``
+    against k, v ``[.., G, 1, K]``)."""
+    return h // (Hq // Hkv)
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
+           slopes=None, rows=None):
+    """Attention of one segment, float64 throughout.
+
+    q ``[M, Hq, D]``, k and v ``[N, Hkv, D]`` (float64). ``rows`` optionally
+    selects which query rows to compute (default all). Returns
+    ``(o [len(rows), Hq, D], lse [Hq, len(rows)])``.
+    """
+    M, Hq, D = q.shape
+    N, Hkv, Dk = k.shape
+    if Dk != D or v.shape != k.shape or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    sc = float(np.float32(scale))
+    i = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    j = np.arange(N)
+    pos_i = i + (N - M)                       # bottom-right aligned query position
+    if causal:
+        allowed = j[None, :] <= pos_i[:, None]
+    else:
+        allowed = np.ones((len(i), N), dtype=bool)
+    any_allowed = allowed.any(axis=1)
+
+    o = np.zeros((len(i), Hq, D), dtype=np.float64)
+    lse = np.full((Hq, len(i)), -np.inf, dtype=np.float64)
+    if N == 0 or len(i) == 0:
+        return o, lse
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        s = sc * (q[i, h, :] @ k[:, g, :].T)
+        if slopes is not None:
+            slope = float(np.float32(slopes[h]))
+            s = s - slope * np.abs(pos_i[:, None] - j[None, :]).astype(np.float64)
+        s = np.where(allowed, s, -np.inf)
+        m = np.where(any_allowed, s.max(axis=1, initial=-np.inf), 0.0)
+        e = np.where(allowed, np.exp(s - m[:, None]), 0.0)
+        l = e.sum(axis=1)
+        safe_l = np.where(l > 0, l, 1.0)
+        o[:, h, :] = np.where(any_allowed[:, None], (e @ v[:, g, :]) / safe_l[:, None], 0.0)
+        lse[h] = np.where(any_allowed, m + np.log(safe_l), -np.inf)
+    return o, lse
+
+
+def _segments(B, M, N, seqstart_q, seqstart_k):
+    if seqstart_q is None:
+        return [(b, 0, M, 0, N) for b in range(B)]
+    sq = np.asarray(seqstart_q, dtype=np.int64)
+    sk = np.asarray(seqstart_k if seqstart_k is not None else seqstart_q, dtype=np.int64)
+    return [(0, int(sq[s]), int(sq[s + 1]), int(sk[s]), int(sk[s + 1])) for s in range(len(sq) - 1)]
+
+
+def fwd(q_bits, k_bits, v_bits, dtype: str, scale: float, causal: bool = False,
+        seqstart_q=None, seqstart_k=None, alibi_slopes=None):
+    """Forward attention over bit-pattern inputs.
+
+    Dense: q ``[B,M,Hq,D]``, k/v ``[B,N,Hkv,D]``. Packed (block-diagonal): q
+    ``[1,T_q,Hq,D]``, k/v ``[1,T_k,Hkv,D]`` and int prefix sums ``seqstart_q``
+    (``seqstart_k`` defaults to it): query segment s sees only key segment s
+    (tutorial section "Utilizzare Sequenze di Lunghezza Variabile",
+    BlockDiagonalMask / BlockDiagonalCausalMask).
+
+    Returns ``(o, lse)``: o float64 shaped like q, lse ``[B, Hq, M]`` (dense)
+    or ``[1, Hq, T_q]`` (packed).
+    """
+    q = decode_bits(q_bits, dtype)
+    k = decode_bits(k_bits, dtype)
+    v = decode_bits(v_bits, dtype)
+    B, M, Hq, D = q.shape
+    N = k.shape[1]
+    o = np.zeros_like(q)
+    lse = np.full((B, Hq, M), -np.inf)
+    for b, q0, q1, k0, k1 in _segments(B, M, N, seqstart_q, seqstart_k):
+        ob, lb = attend(q[b, q0:q1], k[b, k0:k1], v[b, k0:k1], scale, causal, alibi_slopes)
+        o[b, q0:q1] = ob
+        lse[b, :, q0:q1] = lb
+    return o, lse
+
+
+def fwd_rows(q_bits, k_bits, v_bits, dtype: str, scale: float, b: int, rows, causal: bool = False,
+             seqstart_q=None, seqstart_k=None, segment: int | None = None, alibi_slopes=None):
+    """Selected query rows of :func:`fwd` for one batch row ``b`` (dense) or one
+    packed ``segment`` (then ``rows`` are segment-local). Only that batch row
+    or segment is decoded, so this stays cheap at full workload sizes."""
+    if seqstart_q is None:
+        q = decode_bits(q_bits[b], dtype)
+        k = decode_bits(k_bits[b], dtype)
+        v = decode_bits(v_bits[b], dtype)
+    else:
+        sq = np.asarray(seqstart_q, dtype=np.int64)
+        sk = np.asarray(seqstart_k if seqstart_k is not None else seqstart_q, dtype=np.int64)
+        q = decode_bits(q_bits[0, sq[segment]:sq[segment + 1]], dtype)
+        k = decode_bits(k_bits[0, sk[segment]:sk[segment + 1]], dtype)
+        v = decode_bits(v_bits[0, sk[segment]:sk[segment + 1]], dtype)
+    return attend(q, k, v, scale, causal, alibi_slopes, rows=rows)
+
+
+def decode(q_bits, kcache_bits, vcache_bits, ctx_lens, dtype: str, scale: float,
+           alibi_slopes=None, batches=None):
+    """One KV-cache decode step.
+
+    q ``[B,Hq,D]``; caches ``[B,S_max,Hkv,D]``; the query of batch row b sits at
+    position ``ctx_lens[b]-1`` and attends to cache rows ``0..ctx_lens[b]-1``
+    (its own k/v already appended). Rows not in ``batches`` are left NaN.
+    Returns o float64 ``[B,Hq,D]``.
+    """
+    B, Hq, D = q_bits.shape
+    o = np.full((B, Hq, D), np.nan)
+    for b in (range(B) if batches is None else batches):
+        n = int(ctx_lens[b])
+        qb = decode_bits(q_bits[b], dtype)[None]
+        kb = decode_bits(kcache_bits[b, :n], dtype)
+        vb = decode_bits(vcache_bits[b, :n], dtype)
+        ob, _ = attend(qb, kb, vb, scale, causal=True, slopes=alibi_slopes)
+        o[b] = ob[0]
+    return o
