@@ -1,0 +1,137 @@
+/*
+ * mea.h - memory-efficient exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmea.so. Every entry point takes plain pointers and sizes; no
+ * torch or HIP types appear in the signatures (a stream is passed as the
+ * hipStream_t value cast to void*, NULL meaning the null stream).
+ *
+ * Conventions shared by all entry points
+ *   - Tensor pointers are DEVICE pointers, owned by the caller; the library
+ *     never allocates, frees or keeps device memory, and keeps no state
+ *     between calls.
+ *   - Work is enqueued asynchronously on `stream`; no call synchronises.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error the call returns a nonzero status and launches nothing. Contents
+ *     of device arrays (seqstart_*, ctx_lens) cannot be checked without a
+ *     sync; they are a documented precondition, and the kernels clamp every
+ *     row index they derive from them to the tensor bounds, so malformed
+ *     contents give wrong numbers, never out-of-bounds accesses.
+ *   - fp16/bf16 tensors are contiguous, row-major, element strides as stated.
+ *   - Accumulation is fp32; P (the softmax numerators) is rounded to the
+ *     input type before the P.V product; outputs are rounded to nearest even.
+ *   - Stateless and reentrant: calls from several host threads are safe.
+ */
+#ifndef MEA_H
+#define MEA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MEA_OK 0
+#define MEA_EINVAL 1       /* null pointer, non-positive size, inconsistent heads, bad scale */
+#define MEA_EUNSUPPORTED 2 /* (dtype, head dim) combination without a kernel */
+#define MEA_EWORKSPACE 3   /* decode workspace missing or too small */
+#define MEA_EHIP 4         /* the HIP runtime rejected a launch */
+
+/* Element types of q, k, v, caches and outputs. */
+#define MEA_FP16 0
+#define MEA_BF16 1
+
+/* bias_kind bit flags. */
+#define MEA_MASK_CAUSAL 1u    /* query i of a segment with M queries, N keys sees key j iff j <= i + N - M */
+#define MEA_MASK_BLOCKDIAG 2u /* packed segments; each query segment sees only its own key segment */
+#define MEA_BIAS_ALIBI 4u     /* adds -slope[h] * |(i + N - M) - j| to the scaled score */
+
+/*
+ * mea_fwd - exact scaled-dot-product attention forward pass that never forms
+ * the M x N score matrix: Q tiles stay on chip while K/V tiles stream through
+ * LDS and an online softmax (running row max and row sum, rescaled as each
+ * new block arrives) accumulates the output.
+ *
+ * The method: "FlashAttention (2022): l'attenzione che non satura la
+ * memoria" (paithon.it), sections on tiling ("L'idea: non scrivere mai la
+ * matrice intera") and on the online softmax; its API shape and variants
+ * (causal lower-triangular mask, packed variable-length batches under a
+ * block-diagonal mask, grouped-query attention, ALiBi): "Come costruire
+ * Transformer efficienti in memoria con xFormers..." (chipsbuilder.com).
+ *
+ *   out[b,i,h,:] = sum_j softmax_j( scale * q[b,i,h,:].k[b,j,g,:] + bias ) v[b,j,g,:]
+ *   with g = h / (Hq / Hkv), over the keys j the mask allows.
+ *
+ * Layout (dense, bias_kind without MEA_MASK_BLOCKDIAG):
+ *   q, out  [B, M, Hq,  D]      k, v  [B, N, Hkv, D]
+ * Layout (packed, MEA_MASK_BLOCKDIAG): the batch is one physical row,
+ *   q, out  [M, Hq, D]  (M = total packed queries)
+ *   k, v    [N, Hkv, D] (N = total packed keys)
+ *   B is the number of segments; seqstart_q / seqstart_k are int32 device
+ *   arrays of B+1 non-decreasing prefix sums with seqstart_q[0] = 0,
+ *   seqstart_q[B] = M (resp. N). seqstart_k may be NULL: then it equals
+ *   seqstart_q (self-attention, requires M == N).
+ *   Causal alignment is bottom-right within each segment.
+ * scale         > 0 and finite (typically 1/sqrt(D)); used as given in fp32.
+ * alibi_slopes  fp32 device array [Hq], required iff MEA_BIAS_ALIBI is set.
+ * dtype         MEA_FP16 or MEA_BF16 for q, k, v and out.
+ * lse           optional fp32 device array: log-sum-exp of each row's scaled,
+ *               biased scores, natural log; layout [B, Hq, M] (dense) or
+ *               [Hq, M] (packed). -inf for a row with no allowed key. NULL to skip.
+ * Rows with no allowed key get out = 0.
+ * Supported D: 64, 128 (see mea_supported). Hq % Hkv == 0.
+ * Returns MEA_OK or an error status (nothing launched on error).
+ */
+int mea_fwd(const void* q, const void* k, const void* v, void* out,
+            int B, int M, int N, int Hq, int Hkv, int D, float scale,
+            unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
+            const float* alibi_slopes, int dtype, float* lse, void* stream);
+
+/*
+ * mea_decode - one KV-cache decode step: each sequence's newest query
+ * attends to all of its cached keys (its own key and value already
+ * appended). Split-KV: the context is cut into fixed chunks, each chunk
+ * yields a partial (row max, row sum, unnormalised output) for all query
+ * heads of one KV head, and a combine kernel merges the partials by their
+ * log-sum-exp. The step itself: "Transformer : comprendre l'entrainement et
+ * l'inference" (briefia.fr), sections on prefill vs decode and the simple
+ * KV cache; the single-query equivalence: "Transformerを実装して少し理解した
+ * 気になる会(その4)" (scrapbox.io), section "KV Cache"; the merge rule is
+ * the block update of the online softmax (paithon.it page above).
+ *
+ *   q, out   [B, Hq, D]             (one query per sequence)
+ *   kcache   [B, S_max, Hkv, D]     vcache same
+ *   ctx_lens int32 device array [B], 0 <= ctx_lens[b] <= S_max. Slots
+ *            >= ctx_lens[b] are never read and may hold anything (NaN).
+ *            ctx_lens[b] == 0 gives out = 0.
+ *   The query of sequence b sits at position ctx_lens[b]-1 (ALiBi distance
+ *   ctx_lens[b]-1-j).
+ * alibi_slopes  fp32 device array [Hq] or NULL (no bias).
+ * workspace     device buffer of at least mea_decode_workspace_bytes(B, Hq, D,
+ *               S_max) bytes, 256-byte aligned, owned by the caller; its
+ *               contents on entry are ignored. Concurrent calls must not
+ *               share a workspace.
+ * Returns MEA_OK or an error status (nothing launched on error).
+ */
+size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max);
+int mea_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens,
+               void* out, int B, int Hq, int Hkv, int D, int S_max, float scale,
+               const float* alibi_slopes, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* mea_strerror(int status);
+
+/* 1 if (dtype, head dim D) has kernels, else 0 (what xFormers' info listing
+ * of supported kernels answers in the tutorial's setup section). */
+int mea_supported(int dtype, int D);
+
+/* Decode split-KV chunk length in keys (the granularity of the workspace). */
+int mea_decode_chunk(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEA_H */

@@ -1,0 +1,34 @@
+"""Memory-efficient exact attention for AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``libmea.so`` (``include/mea.h``); this package is its thin Python binding:
+
+* :func:`fwd` - tiled exact attention forward (causal, packed block-diagonal,
+  grouped-query, ALiBi);
+* :func:`decode` - one KV-cache decode step (split-KV partials + combine).
+
+Import fails if the library has not been built
+(``python -m memory_efficient_exact_tiled_amd.build``).
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MEA_BF16,
+    MEA_BIAS_ALIBI,
+    MEA_EHIP,
+    MEA_EINVAL,
+    MEA_EUNSUPPORTED,
+    MEA_EWORKSPACE,
+    MEA_FP16,
+    MEA_MASK_BLOCKDIAG,
+    MEA_MASK_CAUSAL,
+    MEA_OK,
+    MeaError,
+    decode,
+    decode_chunk,
+    decode_workspace_bytes,
+    fwd,
+    lib,
+    strerror,
+    supported,
+)

@@ -1,0 +1,177 @@
+"""ctypes binding of libmea.so: the same entry points as include/mea.h.
+
+Argument marshalling only: shapes and dtypes of torch tensors are turned into
+the pointers and sizes of the C ABI, and the current HIP stream is passed
+along. Every step of the computation runs in the library's kernels; there is
+no fallback. Importing this module fails loudly if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+# torch owns the device memory and streams handed to the library, so its HIP
+# runtime must be the one the library binds to: import it before loading
+# libmea.so, whose libamdhip64 dependency then resolves to torch's copy.
+import torch  # noqa: F401
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmea.so")
+
+MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP = 0, 1, 2, 3, 4
+MEA_FP16, MEA_BF16 = 0, 1
+MEA_MASK_CAUSAL, MEA_MASK_BLOCKDIAG, MEA_BIAS_ALIBI = 1, 2, 4
+
+EXPORTS = ("mea_fwd", "mea_decode", "mea_decode_workspace_bytes", "mea_strerror",
+           "mea_supported", "mea_decode_chunk")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m memory_efficient_exact_tiled_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i, _f, _u, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
+_lib.mea_fwd.restype = _i
+_lib.mea_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp, _i, _vp, _vp]
+_lib.mea_decode.restype = _i
+_lib.mea_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _vp]
+_lib.mea_decode_workspace_bytes.restype = _sz
+_lib.mea_decode_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.mea_strerror.restype = ctypes.c_char_p
+_lib.mea_strerror.argtypes = [_i]
+_lib.mea_supported.restype = _i
+_lib.mea_supported.argtypes = [_i, _i]
+_lib.mea_decode_chunk.restype = _i
+_lib.mea_decode_chunk.argtypes = []
+
+
+class MeaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"mea status {status}: {_lib.mea_strerror(status).decode()}")
+
+
+def lib():
+    """The loaded ctypes library (for callers that pass raw pointers)."""
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return _lib.mea_strerror(status).decode()
+
+
+def supported(dtype_code: int, D: int) -> bool:
+    return bool(_lib.mea_supported(dtype_code, D))
+
+
+def decode_chunk() -> int:
+    return int(_lib.mea_decode_chunk())
+
+
+def decode_workspace_bytes(B: int, Hq: int, D: int, S_max: int) -> int:
+    return int(_lib.mea_decode_workspace_bytes(B, Hq, D, S_max))
+
+
+def _check(status: int) -> None:
+    if status != MEA_OK:
+        raise MeaError(status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return MEA_FP16
+    if t.dtype == torch.bfloat16:
+        return MEA_BF16
+    raise TypeError(f"q/k/v must be float16 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def fwd(q, k, v, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alibi_slopes=None,
+        scale: float | None = None, out=None, lse=None, stream=None):
+    """Exact attention forward (``mea_fwd``).
+
+    Dense: q ``[B,M,Hq,D]``, k/v ``[B,N,Hkv,D]``. Packed (``seqstart_q`` given):
+    q ``[1,M,Hq,D]`` (or ``[M,Hq,D]``), k/v ``[1,N,Hkv,D]``, int32 prefix sums
+    ``seqstart_q`` (``seqstart_k`` defaults to it) on the device. ``lse`` (fp32,
+    ``[B,Hq,M]`` / ``[Hq,M]``) is filled if given. Returns ``out``.
+    """
+    torch = _torch()
+    varlen = seqstart_q is not None
+    if varlen:
+        qv = q.reshape(-1, q.shape[-2], q.shape[-1])
+        kv_ = k.reshape(-1, k.shape[-2], k.shape[-1])
+        M, Hq, D = qv.shape
+        N, Hkv, _ = kv_.shape
+        B = seqstart_q.numel() - 1
+        for s in (seqstart_q, seqstart_k):
+            if s is not None and (s.dtype != torch.int32 or not s.is_cuda):
+                raise TypeError("seqstart arrays must be int32 device tensors")
+    else:
+        B, M, Hq, D = q.shape
+        Bk, N, Hkv, Dk = k.shape
+        if Bk != B or Dk != D:
+            raise ValueError("q and k shapes disagree")
+    if v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match in shape and dtype, and q, k, v in dtype")
+    _need_cuda(q, k, v, out, lse, alibi_slopes)
+    if out is None:
+        out = torch.empty_like(q)
+    if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
+        raise TypeError("alibi_slopes must be float32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kind = ((MEA_MASK_CAUSAL if causal else 0) | (MEA_MASK_BLOCKDIAG if varlen else 0)
+            | (MEA_BIAS_ALIBI if alibi_slopes is not None else 0))
+    _check(_lib.mea_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, M, N, Hq, Hkv, D, float(scale), kind,
+                        _ptr(seqstart_q), _ptr(seqstart_k), _ptr(alibi_slopes), _dtype_code(q), _ptr(lse),
+                        _stream(stream)))
+    return out
+
+
+def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, alibi_slopes=None, out=None,
+           workspace=None, stream=None):
+    """One KV-cache decode step (``mea_decode``): q ``[B,Hq,D]``, caches
+    ``[B,S_max,Hkv,D]``, int32 ``ctx_lens`` ``[B]`` on the device. The workspace
+    is allocated with torch when not given. Returns ``out`` ``[B,Hq,D]``."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Bc, S_max, Hkv, Dc = kcache.shape
+    if Bc != B or Dc != D or vcache.shape != kcache.shape:
+        raise ValueError("q and cache shapes disagree")
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise ValueError("q and caches must share a dtype")
+    if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
+        raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_cuda(q, kcache, vcache, ctx_lens, out, alibi_slopes, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, D, S_max)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(_lib.mea_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(ctx_lens), _ptr(out), B, Hq, Hkv, D, S_max,
+                           float(scale), _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

@@ -1,0 +1,201 @@
+// C ABI of libmea.so (declared in include/mea.h): host-side validation,
+// launch geometry, status codes. Validation happens before any HIP call, so
+// an invalid call touches neither the device nor the runtime.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mea.h"
+#include "launch.hpp"
+
+namespace {
+
+bool mea_debug() {
+  static const bool on = [] {
+    const char* e = std::getenv("MEA_DEBUG");
+    return e != nullptr && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+bool dtype_ok(int dtype) { return dtype == MEA_FP16 || dtype == MEA_BF16; }
+bool dim_ok(int D) { return D == 64 || D == 128; }
+
+// Validates device-resident index arrays with a synchronous copy (MEA_DEBUG=1 only).
+int debug_check_seqstart(const int32_t* st, int B, int total, hipStream_t stream) {
+  int32_t* h = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * (size_t)(B + 1)));
+  if (h == nullptr) return MEA_EINVAL;
+  int rc = MEA_OK;
+  if (hipMemcpyAsync(h, st, sizeof(int32_t) * (size_t)(B + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    rc = MEA_EHIP;
+  } else {
+    if (h[0] != 0 || h[B] != total) rc = MEA_EINVAL;
+    for (int s = 0; s < B && rc == MEA_OK; ++s)
+      if (h[s + 1] < h[s]) rc = MEA_EINVAL;
+  }
+  std::free(h);
+  return rc;
+}
+
+int debug_check_ctx(const int32_t* ctx, int B, int S_max, hipStream_t stream) {
+  int32_t* h = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * (size_t)B));
+  if (h == nullptr) return MEA_EINVAL;
+  int rc = MEA_OK;
+  if (hipMemcpyAsync(h, ctx, sizeof(int32_t) * (size_t)B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    rc = MEA_EHIP;
+  } else {
+    for (int b = 0; b < B && rc == MEA_OK; ++b)
+      if (h[b] < 0 || h[b] > S_max) rc = MEA_EINVAL;
+  }
+  std::free(h);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mea_strerror(int status) {
+  switch (status) {
+    case MEA_OK: return "success";
+    case MEA_EINVAL: return "invalid argument";
+    case MEA_EUNSUPPORTED: return "unsupported dtype or head dimension";
+    case MEA_EWORKSPACE: return "decode workspace missing or too small";
+    case MEA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mea_supported(int dtype, int D) { return (dtype_ok(dtype) && dim_ok(D)) ? 1 : 0; }
+
+int mea_decode_chunk(void) { return mea::kDecodeChunk; }
+
+int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv, int D,
+            float scale, unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
+            const float* alibi_slopes, int dtype, float* lse, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return MEA_EINVAL;
+  if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return MEA_EINVAL;
+  if (Hq % Hkv != 0) return MEA_EINVAL;
+  if ((bias_kind & ~(MEA_MASK_CAUSAL | MEA_MASK_BLOCKDIAG | MEA_BIAS_ALIBI)) != 0u) return MEA_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return MEA_EINVAL;
+  const bool varlen = (bias_kind & MEA_MASK_BLOCKDIAG) != 0u;
+  const bool causal = (bias_kind & MEA_MASK_CAUSAL) != 0u;
+  const bool alibi = (bias_kind & MEA_BIAS_ALIBI) != 0u;
+  if (alibi && alibi_slopes == nullptr) return MEA_EINVAL;
+  if (varlen) {
+    if (seqstart_q == nullptr) return MEA_EINVAL;
+    if (seqstart_k == nullptr && M != N) return MEA_EINVAL;
+  }
+  if (!mea_supported(dtype, D)) return MEA_EUNSUPPORTED;
+  // Row strides and per-row offsets are int32 inside the kernel; whole-tensor
+  // offsets are 64-bit.
+  const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
+  if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
+  const int BM = mea::fwd_block_m(D);
+
+  mea::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.seqstart_q = seqstart_q;
+  p.seqstart_k = seqstart_k != nullptr ? seqstart_k : seqstart_q;
+  p.slopes = alibi_slopes;
+  p.B = B;
+  p.M = M;
+  p.N = N;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.varlen = varlen;
+  p.alibi = alibi;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q_rstride = (int)q_rstride;
+  p.kv_rstride = (int)kv_rstride;
+  long long tiles, total;
+  if (varlen) {
+    tiles = ((long long)M + BM - 1) / BM + B;   // each segment wastes at most one partial tile
+    total = tiles * Hq;
+    p.q_bstride = 0;
+    p.kv_bstride = 0;
+  } else {
+    tiles = ((long long)M + BM - 1) / BM;
+    total = tiles * Hq * (long long)B;
+    p.q_bstride = (long long)M * q_rstride;
+    p.kv_bstride = (long long)N * kv_rstride;
+  }
+  if (total > 0x7fffffffLL - 8) return MEA_EINVAL;
+  p.n_qtiles = (int)tiles;
+  p.total_wg = (int)total;
+  p.wg_per_xcd = (int)((total + 7) / 8);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mea_debug() && varlen) {
+    int rc = debug_check_seqstart(seqstart_q, B, M, st);
+    if (rc == MEA_OK && seqstart_k != nullptr) rc = debug_check_seqstart(seqstart_k, B, N, st);
+    if (rc != MEA_OK) return rc;
+  }
+  return mea::launch_fwd(dtype, D, p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
+}
+
+size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
+  const size_t nchunk = ((size_t)S_max + mea::kDecodeChunk - 1) / mea::kDecodeChunk;
+  const size_t slots = (size_t)B * (size_t)Hq * nchunk;
+  size_t o_bytes = slots * (size_t)D * sizeof(float);
+  o_bytes = (o_bytes + 255) & ~(size_t)255;
+  return o_bytes + slots * 2 * sizeof(float);
+}
+
+int mea_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
+               int Hq, int Hkv, int D, int S_max, float scale, const float* alibi_slopes, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || kcache == nullptr || vcache == nullptr || ctx_lens == nullptr || out == nullptr)
+    return MEA_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || S_max <= 0) return MEA_EINVAL;
+  if (Hq % Hkv != 0) return MEA_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return MEA_EINVAL;
+  if (!mea_supported(dtype, D)) return MEA_EUNSUPPORTED;
+  if ((long long)Hkv * D > 0x7fffffffLL) return MEA_EINVAL;
+  const size_t need = mea_decode_workspace_bytes(B, Hq, D, S_max);
+  if (workspace == nullptr || workspace_bytes < need) return MEA_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return MEA_EWORKSPACE;
+  const long long nchunk = ((long long)S_max + mea::kDecodeChunk - 1) / mea::kDecodeChunk;
+  const int group = Hq / Hkv;
+  const int nhb = (group + 15) / 16;
+  if (nchunk > 0x7fffffffLL || (long long)Hkv * nhb > 65535 || B > 65535) return MEA_EINVAL;
+
+  mea::DecParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = static_cast<const uint16_t*>(kcache);
+  p.vc = static_cast<const uint16_t*>(vcache);
+  p.ctx = ctx_lens;
+  p.out = static_cast<uint16_t*>(out);
+  p.slopes = alibi_slopes;
+  const size_t slots = (size_t)B * (size_t)Hq * (size_t)nchunk;
+  size_t o_bytes = (slots * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = group;
+  p.S_max = S_max;
+  p.nchunk = (int)nchunk;
+  p.nhb = nhb;
+  p.alibi = alibi_slopes != nullptr;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mea_debug()) {
+    const int rc = debug_check_ctx(ctx_lens, B, S_max, st);
+    if (rc != MEA_OK) return rc;
+  }
+  return mea::launch_decode(dtype, D, p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, MFMA
+// wrappers and the LDS transpose read.
+//
+// Operand layouts used throughout (wave64, verified on gfx950):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A lane l holds row l%32, k = (l/32)*8 + 0..7;
+//     B lane l holds column l%32, same k; C/D lane l holds column l%32 and
+//     rows (r/4)*8 + (l/32)*4 + r%4 for r = 0..15.
+//   v_mfma_f32_16x16x32_{bf16,f16}: A lane l holds row l%16, k = (l/16)*8 + 0..7;
+//     B lane l holds column l%16, same k; C/D lane l holds column l%16 and rows
+//     (l/16)*4 + r for r = 0..3.
+//   ds_read_b64_tr_b16: within each group of 16 lanes, lane s addresses 8 bytes
+//     (4 elements); lane s of the result receives element (s % 4) of the
+//     addresses given by lanes 4*j + s/4, j = 0..3, i.e. when the 16 lanes
+//     address a 4-row x 16-column block of a row-major tile (lane s: row s/4,
+//     columns 4*(s%4)..+3), lane s gets column s of rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mea {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ f32x16 mma32(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<_Float16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ f32x16 mma32(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Eight elements from two transpose reads of LDS (see the layout note above).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::v8 lds_tr_x8(const uint16_t* p0, const uint16_t* p1) {
+  typedef typename Mfma<T>::v4 v4;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  v4 x = __builtin_bit_cast(v4, a);
+  v4 y = __builtin_bit_cast(v4, b);
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::v8 load_v8(const uint16_t* p) {
+  return __builtin_bit_cast(typename Mfma<T>::v8, *reinterpret_cast<const uint4*>(p));
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::v8 zero_v8() {
+  return __builtin_bit_cast(typename Mfma<T>::v8, make_uint4(0u, 0u, 0u, 0u));
+}
+
+// 2^x on the transcendental unit (v_exp_f32): exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_xor(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask)); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescaling: the running row maximum is only raised when a block's
+// maximum exceeds it by more than this many powers of two, so P <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+}  // namespace mea

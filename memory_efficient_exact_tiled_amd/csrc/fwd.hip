@@ -1,0 +1,332 @@
+// Tiled exact attention forward pass for gfx950 (MI355X).
+//
+// Method: the score matrix is never formed. Each work-group keeps a block of
+// queries on chip, streams K/V blocks of the same (segment, KV head) through
+// LDS, and folds every block into an online softmax: a running row maximum
+// and row sum, with the accumulated output rescaled when the maximum grows.
+// Only the output (and optionally the row log-sum-exp) is written back.
+// ("FlashAttention (2022): l'attenzione che non satura la memoria",
+// paithon.it, sections on tiling and on the online softmax.)
+//
+// Work decomposition (one work-group = 4 waves = 256 threads):
+//   * a work-group owns BM = 4 * 32 * QB query rows of one (batch or packed
+//     segment, query head); wave w owns 32 * QB consecutive rows;
+//   * K/V blocks of BN = 64 keys are copied HBM -> registers -> LDS, double
+//     buffered so one barrier per block suffices; the next block's global
+//     loads are in flight while the current block is computed;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
+//     registers for the whole kernel). With this orientation each lane holds
+//     one query's scores for 32 of the 64 keys, so the row max needs a single
+//     cross-lane step (lane l and l^32) and the row sum none until the end;
+//   * P^T is rounded to the input type in registers and fed straight back as
+//     the B operand of O^T = V^T P^T; V^T comes from the row-major V block
+//     with ds_read_b64_tr_b16, which matches the key order P^T has in the
+//     score accumulators, so V is never transposed in memory;
+//   * causal and block-diagonal masks are index predicates evaluated only on
+//     blocks that straddle the diagonal or the segment end; blocks entirely
+//     above the diagonal are never visited (per work-group) or computed (per
+//     wave); ALiBi is computed from the indices;
+//   * grouped-query attention: query head h reads KV head h / (Hq / Hkv) in
+//     place; the heads sharing a KV head are adjacent in the launch order.
+//
+// Launch order: work-group p runs on XCD p % 8; each XCD is given a
+// contiguous range of logical work-groups, so the query tiles of one head
+// (which read the same K/V) share that XCD's L2. Under a causal mask the
+// tiles of a head are issued longest first.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mea {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBN = 64;
+
+template <int D>
+struct FwdShape {
+  static constexpr int QB = 2;                  // 32-row query blocks per wave
+  static constexpr int QW = 32 * QB;            // query rows per wave
+  static constexpr int BM = kWaves * QW;        // query rows per work-group
+  static constexpr int LDS = D + 16;            // padded LDS row stride (elements)
+  static constexpr int TILE = kBN * LDS;        // elements of one K or V block
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int NLD = kBN * CPR / (kWaves * 64);  // chunks per thread per tensor
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) fwd_kernel(const FwdParams p) {
+  using S = FwdShape<D>;
+  using MF = Mfma<T>;
+  typedef typename MF::v8 v8;
+  constexpr int QB = S::QB, QW = S::QW, BM = S::BM, LDS = S::LDS, TILE = S::TILE;
+  constexpr int CPR = S::CPR, NLD = S::NLD;
+  constexpr int DB = D / 32;   // 32-wide output column blocks
+  constexpr int DS = D / 16;   // k-steps of the score product
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- work decomposition -------------------------------------------------
+  const int pid = blockIdx.x;
+  const int lid = (pid & 7) * p.wg_per_xcd + (pid >> 3);
+  if (lid >= p.total_wg) return;
+  const int bh = lid / p.n_qtiles;
+  const int t = lid - bh * p.n_qtiles;
+  const int h = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int g = h / p.group;
+
+  int M_s, N_s, tile;
+  long long qoff, koff, lse_off;
+  if (!p.varlen) {
+    M_s = p.M;
+    N_s = p.N;
+    tile = p.causal ? (p.n_qtiles - 1 - t) : t;
+    qoff = (long long)b * p.q_bstride + (long long)h * D;
+    koff = (long long)b * p.kv_bstride + (long long)g * D;
+    lse_off = ((long long)b * p.Hq + h) * p.M;
+  } else {
+    // Locate (segment, tile) by scanning the segment boundaries; boundaries
+    // are clamped to the tensor extents so no row index can leave them.
+    int acc = 0, s = 0, a0 = 0, a1 = 0, ntile = 0;
+    for (; s < p.B; ++s) {
+      a0 = min(max(p.seqstart_q[s], 0), p.M);
+      a1 = min(max(p.seqstart_q[s + 1], a0), p.M);
+      ntile = (a1 - a0 + BM - 1) / BM;
+      if (t < acc + ntile) break;
+      acc += ntile;
+    }
+    if (s >= p.B) return;
+    const int in = t - acc;
+    tile = p.causal ? (ntile - 1 - in) : in;
+    const int* sk = p.seqstart_k;
+    const int k0 = min(max(sk[s], 0), p.N);
+    const int k1 = min(max(sk[s + 1], k0), p.N);
+    M_s = a1 - a0;
+    N_s = k1 - k0;
+    qoff = (long long)a0 * p.q_rstride + (long long)h * D;
+    koff = (long long)k0 * p.kv_rstride + (long long)g * D;
+    lse_off = (long long)h * p.M + a0;
+  }
+
+  const int i0 = tile * BM;            // first query row of the work-group (segment-local)
+  const int off = N_s - M_s;           // bottom-right causal alignment
+  int kend = N_s;
+  if (p.causal) kend = min(N_s, i0 + BM + off);
+  kend = max(kend, 0);
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  const int wq0 = i0 + wave * QW;      // first query row of this wave
+  const int wlast = min(wq0 + QW, M_s) - 1;
+  int wkend = 0;                       // keys this wave needs
+  if (wlast >= wq0) wkend = p.causal ? max(min(N_s, wlast + off + 1), 0) : N_s;
+
+  const float c = p.scale_log2;
+  const float slope = p.alibi ? p.slopes[h] * kLog2e : 0.f;
+
+  // ---- Q fragments (B operand: column = query, k = head dim) ---------------
+  v8 qf[QB][DS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wq0 + qb * 32 + l32;
+#pragma unroll
+    for (int st = 0; st < DS; ++st)
+      qf[qb][st] = (row < M_s) ? load_v8<T>(p.q + qoff + (long long)row * p.q_rstride + st * 16 + hi * 8)
+                               : zero_v8<T>();
+  }
+
+  f32x16 o[QB][DB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+  }
+
+  // ---- K/V staging ---------------------------------------------------------
+  uint4 kst[NLD], vst[NLD];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int ch = tid + i * (kWaves * 64);
+      const int r = ch / CPR;
+      const int cc = (ch - r * CPR) * 8;
+      const int key = kt * kBN + r;
+      if (key < N_s) {
+        const long long e = koff + (long long)key * p.kv_rstride + cc;
+        kst[i] = *reinterpret_cast<const uint4*>(p.k + e);
+        vst[i] = *reinterpret_cast<const uint4*>(p.v + e);
+      } else {
+        kst[i] = make_uint4(0u, 0u, 0u, 0u);
+        vst[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* ks = smem + buf * 2 * TILE;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int ch = tid + i * (kWaves * 64);
+      const int r = ch / CPR;
+      const int cc = (ch - r * CPR) * 8;
+      *reinterpret_cast<uint4*>(ks + r * LDS + cc) = kst[i];
+      *reinterpret_cast<uint4*>(ks + TILE + r * LDS + cc) = vst[i];
+    }
+  };
+
+  // Lane coordinates of the V^T transpose reads.
+  const int g16 = lane >> 4;
+  const int ll = lane & 15;
+  const int vrow = (g16 >> 1) * 4 + (ll >> 2);
+  const int vcol = (g16 & 1) * 16 + 4 * (ll & 3);
+
+  if (ntiles > 0) gload(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    lstore(buf);
+    __syncthreads();
+    if (kt + 1 < ntiles) gload(kt + 1);
+
+    const int key_base = kt * kBN;
+    if (key_base >= wkend) continue;   // the whole block is masked for this wave
+    const uint16_t* Ks = smem + buf * 2 * TILE;
+    const uint16_t* Vs = Ks + TILE;
+
+    // S^T = K Q^T
+    f32x16 s[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const v8 kf = load_v8<T>(Ks + (kb * 32 + l32) * LDS + st * 16 + hi * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = MF::mma32(kf, qf[qb][st], s[qb][kb]);
+      }
+    }
+
+    const bool need_mask = (key_base + kBN > N_s) || (p.causal && key_base + kBN - 1 > wq0 + off);
+    typename MF::v8 pf[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = wq0 + qb * 32 + l32;
+      float cc = c;
+      if (p.alibi || need_mask) {
+        // Explicit scores in log2 units: scale, ALiBi from indices, mask.
+        const int rel = key_base + hi * 4;           // key = rel + kr
+        const int lim_n = N_s - rel;                 // kr <  lim_n : inside the segment
+        const int lim_c = p.causal ? (qi + off - rel) : 0x7fffffff;  // kr <= lim_c : causal
+        const float dist0 = (float)(qi + off - rel);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
+            float x = s[qb][kb][r] * c;
+            if (p.alibi) x -= slope * fabsf(dist0 - (float)kr);
+            s[qb][kb][r] = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
+          }
+        cc = 1.f;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      mx = wave_max_xor(mx, 32);
+      const float mt = mx * cc;
+      if (__any(mt > m_run[qb] + kRescaleThreshold)) {
+        const float mn = fmaxf(m_run[qb], mt);
+        const float alpha = fast_exp2(m_run[qb] - (mn == -INFINITY ? 0.f : mn));
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+        m_run[qb] = mn;
+      }
+      const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(s[qb][kb][r], cc, -mu));
+          s[qb][kb][r] = pv;
+          psum += pv;
+        }
+      l_run[qb] += psum;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pf[qb][tt][u] = (T)s[qb][tt >> 1][(tt & 1) * 8 + u];
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const uint16_t* a0 = Vs + (tt * 16 + vrow) * LDS + db * 32 + vcol;
+        const v8 vf = lds_tr_x8<T>(a0, a0 + 8 * LDS);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[qb][db] = MF::mma32(vf, pf[qb][tt], o[qb][db]);
+      }
+    }
+  }
+
+  // ---- epilogue --------------------------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const int qi = wq0 + qb * 32 + l32;
+    if (qi < M_s) {
+      const float inv = lt != 0.f ? 1.f / lt : 0.f;   // no allowed key -> 0; NaN stays NaN
+      uint16_t* orow = p.out + qoff + (long long)qi * p.q_rstride;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          typename MF::v4 w;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) w[u] = (T)(o[qb][db][rg * 4 + u] * inv);
+          *reinterpret_cast<uint2*>(orow + db * 32 + rg * 8 + hi * 4) = __builtin_bit_cast(uint2, w);
+        }
+      if (p.lse != nullptr && hi == 0)
+        p.lse[lse_off + qi] = lt != 0.f ? (m_run[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
+  const int grid = p.wg_per_xcd * 8;
+  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int fwd_block_m(int D) { return D == 64 ? FwdShape<64>::BM : FwdShape<128>::BM; }
+
+hipError_t launch_fwd(int dtype, int D, const FwdParams& p, hipStream_t stream) {
+  if (dtype == 0) return D == 64 ? launch_typed<_Float16, 64>(p, stream) : launch_typed<_Float16, 128>(p, stream);
+  return D == 64 ? launch_typed<__bf16, 64>(p, stream) : launch_typed<__bf16, 128>(p, stream);
+}
+
+}  // namespace mea

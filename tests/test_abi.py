@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every symbol include/mea.h declares, and
+rejects invalid calls on the host before touching the device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_efficient_exact_tiled_amd as mea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mea.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mea_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(mea.LIB_PATH)
+    names = _declared()
+    assert set(names) == set(mea.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_and_supported():
+    assert mea.strerror(0) == "success"
+    for s in range(1, 5):
+        assert mea.strerror(s) and mea.strerror(s) != "unknown status"
+    assert mea.strerror(99) == "unknown status"
+    for dt in (mea.MEA_FP16, mea.MEA_BF16):
+        assert mea.supported(dt, 64) and mea.supported(dt, 128)
+        assert not mea.supported(dt, 96) and not mea.supported(dt, 256)
+    assert not mea.supported(7, 64)
+
+
+def test_workspace_bytes():
+    C = mea.decode_chunk()
+    assert C == 512
+    nch = (32768 + C - 1) // C
+    o = 32 * 32 * nch * 128 * 4
+    assert mea.decode_workspace_bytes(32, 32, 128, 32768) == ((o + 255) // 256) * 256 + 32 * 32 * nch * 2 * 4
+    assert mea.decode_workspace_bytes(0, 32, 128, 32768) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, M=8, N=8, Hq=2, Hkv=1, D=64, scale=0.125, kind=0,
+             sq=None, sk=None, sl=None, dtype=mea.MEA_BF16, lse=None, stream=None)
+    a.update(kw)
+    return mea.lib().mea_fwd(a["q"], a["k"], a["v"], a["out"], a["B"], a["M"], a["N"], a["Hq"], a["Hkv"], a["D"],
+                             a["scale"], a["kind"], a["sq"], a["sk"], a["sl"], a["dtype"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mea.MEA_EINVAL),
+    (dict(out=None), mea.MEA_EINVAL),
+    (dict(B=0), mea.MEA_EINVAL),
+    (dict(M=-1), mea.MEA_EINVAL),
+    (dict(N=0), mea.MEA_EINVAL),
+    (dict(Hq=3, Hkv=2), mea.MEA_EINVAL),
+    (dict(scale=0.0), mea.MEA_EINVAL),
+    (dict(scale=-0.5), mea.MEA_EINVAL),
+    (dict(scale=float("nan")), mea.MEA_EINVAL),
+    (dict(scale=float("inf")), mea.MEA_EINVAL),
+    (dict(kind=8), mea.MEA_EINVAL),
+    (dict(kind=mea.MEA_BIAS_ALIBI), mea.MEA_EINVAL),
+    (dict(kind=mea.MEA_MASK_BLOCKDIAG), mea.MEA_EINVAL),
+    (dict(kind=mea.MEA_MASK_BLOCKDIAG, sq=FAKE, M=8, N=9), mea.MEA_EINVAL),
+    (dict(D=96), mea.MEA_EUNSUPPORTED),
+    (dict(dtype=5), mea.MEA_EUNSUPPORTED),
+])
+def test_fwd_rejects(kw, status):
+    assert _fwd(**kw) == status
+
+
+def _dec(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ctx=FAKE, out=FAKE, B=2, Hq=4, Hkv=2, D=128, S=1024, scale=0.1, sl=None,
+             dtype=mea.MEA_FP16, ws=ctypes.c_void_p(0x100000), wsb=1 << 30, stream=None)
+    a.update(kw)
+    return mea.lib().mea_decode(a["q"], a["kc"], a["vc"], a["ctx"], a["out"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                a["S"], a["scale"], a["sl"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ctx=None), mea.MEA_EINVAL),
+    (dict(kc=None), mea.MEA_EINVAL),
+    (dict(B=0), mea.MEA_EINVAL),
+    (dict(S=0), mea.MEA_EINVAL),
+    (dict(Hq=6, Hkv=4), mea.MEA_EINVAL),
+    (dict(scale=-1.0), mea.MEA_EINVAL),
+    (dict(D=32), mea.MEA_EUNSUPPORTED),
+    (dict(ws=None), mea.MEA_EWORKSPACE),
+    (dict(wsb=16), mea.MEA_EWORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), mea.MEA_EWORKSPACE),
+])
+def test_decode_rejects(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_product_package_does_not_reach_the_oracle():
+    """The product package neither imports nor names the oracle."""
+    pkg = os.path.join(ROOT, "memory_efficient_exact_tiled_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_single_hip_runtime_in_process():
+    """The library binds to the HIP runtime torch already loaded (one copy of
+    libamdhip64 in the process, whatever the import order)."""
+    import subprocess
+    import sys
+    code = ("import memory_efficient_exact_tiled_amd, torch;"
+            "m=open('/proc/self/maps').read();"
+            "print(len(set(l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l)))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"

@@ -1,0 +1,195 @@
+"""Parity of the HIP forward kernel (through the C ABI) with the fp64 oracle, on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import mea_inputs as inp
+import oracle.attention as orc
+from gpu_util import TOL, dev, f32, host_bits, host_f64, i32, report, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_efficient_exact_tiled_amd as m
+    return m
+
+
+def _run(mea, c, dt, causal=False, slopes=None, st=None, scale=None, with_lse=False):
+    q, k, v = dev(c["q"], dt), dev(c["k"], dt), dev(c["v"], dt)
+    D = c["q"].shape[-1]
+    scale = float(np.float32(1.0 / np.sqrt(D))) if scale is None else scale
+    lse = None
+    if with_lse:
+        B, M, Hq, _ = c["q"].shape
+        lse = torch.full((B, Hq, M) if st is None else (Hq, M), 7.0, dtype=torch.float32, device="cuda")
+    out = mea.fwd(q, k, v, causal=causal, scale=scale,
+                  alibi_slopes=None if slopes is None else f32(slopes),
+                  seqstart_q=None if st is None else i32(st), lse=lse)
+    torch.cuda.synchronize()
+    return out, lse, scale
+
+
+DENSE = [
+    # name, seed, B, M, N, Hq, Hkv, D, dtype, causal
+    ("cfg1_b1_m128_h2_d64_fp16", 0, 1, 128, 128, 2, 2, 64, "fp16", False),
+    ("cfg2_b2_m256_h8_d64_fp16_causal", 1, 2, 256, 256, 8, 8, 64, "fp16", True),
+    ("cfg3_m512_noncausal", 2, 4, 512, 512, 16, 16, 64, "bf16", False),
+    ("cfg3_m512_causal", 2, 4, 512, 512, 16, 16, 64, "bf16", True),
+    ("cfg3_m1024_noncausal", 3, 4, 1024, 1024, 16, 16, 64, "bf16", False),
+    ("cfg3_m1024_causal", 3, 4, 1024, 1024, 16, 16, 64, "bf16", True),
+    ("ragged_m300_n177_d128_bf16", 4, 2, 300, 177, 4, 2, 128, "bf16", False),
+    ("ragged_causal_m333_d128_fp16_gqa", 5, 1, 333, 333, 8, 2, 128, "fp16", True),
+    ("chunked_prefill_m70_n500_causal", 6, 2, 70, 500, 4, 4, 64, "bf16", True),
+    ("more_queries_than_keys_causal", 7, 1, 200, 90, 2, 1, 128, "bf16", True),
+    ("tiny_m1_n1", 8, 3, 1, 1, 2, 2, 64, "fp16", False),
+    ("single_query_n777", 9, 2, 1, 777, 4, 1, 128, "bf16", True),
+    ("gqa_tutorial_b2_m256_hq8_hkv2_d64_fp16", 10, 2, 256, 256, 8, 2, 64, "fp16", False),
+]
+
+
+@pytest.mark.parametrize("case", DENSE, ids=lambda c: c[0])
+def test_dense_parity(mea, case):
+    name, seed, B, M, N, Hq, Hkv, D, dt, causal = case
+    say(f"case {name}")
+    c = inp.dense_case(seed, B, M, N, Hq, Hkv, D, dt)
+    out, lse, scale = _run(mea, c, dt, causal=causal, with_lse=True)
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=causal)
+    err = report(name, host_f64(out), want, TOL[dt])
+    assert err <= TOL[dt]
+    got_lse = lse.cpu().numpy()
+    fin = np.isfinite(wlse)
+    assert np.array_equal(np.isfinite(got_lse), fin), "lse -inf pattern"
+    assert np.max(np.abs(got_lse[fin] - wlse[fin]), initial=0.0) < 1e-3, "lse"
+
+
+@pytest.mark.parametrize("M", [2048, 4096])
+@pytest.mark.parametrize("causal", [False, True])
+def test_seqlen_sweep_sampled(mea, M, causal):
+    """Sequence-length sweep at full size (B=4, H=16, D=64, bf16): the oracle
+    checks a sample of rows of two batch rows, all heads."""
+    name = f"cfg3_m{M}_{'causal' if causal else 'noncausal'}"
+    say(f"case {name}")
+    c = inp.dense_case(11 + M, 4, M, M, 16, 16, 64, "bf16")
+    out, _, scale = _run(mea, c, "bf16", causal=causal)
+    got = host_f64(out)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, M - 1], rng.integers(0, M, 40)]))
+    for b in (0, 3):
+        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], "bf16", scale, b, rows, causal=causal)
+        assert report(f"{name} b{b}", got[b, rows], want, TOL["bf16"]) <= TOL["bf16"]
+
+
+def test_varlen_gqa_alibi_full_config(mea):
+    """8 packed segments, lengths uniform in [64, 2048] (seeded), Hq=32, Hkv=8,
+    D=128, bf16, block-diagonal causal + ALiBi: sampled rows of every segment."""
+    lengths = inp.segment_lengths(4, 8, 64, 2048)
+    say(f"case cfg4 lengths={lengths.tolist()}")
+    c = inp.varlen_case(4, lengths, 32, 8, 128, "bf16")
+    slopes = inp.alibi_slopes(32)
+    out, _, scale = _run(mea, c, "bf16", causal=True, slopes=slopes, st=c["seqstart"])
+    got = host_f64(out)
+    st = c["seqstart"]
+    rng = np.random.default_rng(5)
+    for s, L in enumerate(lengths):
+        rows = np.unique(np.concatenate([[0, 1, L - 1], rng.integers(0, L, 12)]))
+        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], "bf16", scale, 0, rows, causal=True,
+                               seqstart_q=st, segment=s, alibi_slopes=slopes)
+        assert report(f"cfg4 seg{s} L={L}", got[0, st[s] + rows], want, TOL["bf16"]) <= TOL["bf16"]
+
+
+VARLEN = [
+    # name, lengths, Hq, Hkv, D, dtype, causal, alibi
+    ("ragged_segments_causal_alibi_d128", [1, 63, 64, 65, 130, 7, 256, 257], 8, 2, 128, "bf16", True, True),
+    ("ragged_segments_noncausal_d64_fp16", [5, 300, 1, 129], 4, 4, 64, "fp16", False, False),
+    ("ragged_segments_noncausal_alibi", [40, 100, 3], 4, 1, 64, "bf16", False, True),
+    ("one_segment", [513], 2, 1, 128, "fp16", True, False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: c[0])
+def test_varlen_parity_full(mea, case):
+    name, lengths, Hq, Hkv, D, dt, causal, alibi = case
+    say(f"case {name}")
+    c = inp.varlen_case(21, lengths, Hq, Hkv, D, dt)
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    out, lse, scale = _run(mea, c, dt, causal=causal, slopes=slopes, st=c["seqstart"], with_lse=True)
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=causal, seqstart_q=c["seqstart"],
+                         alibi_slopes=slopes)
+    assert report(name, host_f64(out), want, TOL[dt]) <= TOL[dt]
+    assert np.max(np.abs(lse.cpu().numpy() - wlse[0])) < 1e-3
+
+
+def test_varlen_equals_per_segment_bitwise(mea):
+    """Block-diagonal output equals per-segment calls bit for bit (tiles start
+    at segment starts, so the arithmetic is the same)."""
+    lengths = [70, 1, 300, 129]
+    c = inp.varlen_case(31, lengths, 8, 2, 128, "bf16")
+    slopes = inp.alibi_slopes(8)
+    out, _, _ = _run(mea, c, "bf16", causal=True, slopes=slopes, st=c["seqstart"])
+    got = host_bits(out)
+    st = c["seqstart"]
+    for s in range(len(lengths)):
+        a, b = st[s], st[s + 1]
+        seg = {key: c[key][:, a:b] for key in ("q", "k", "v")}
+        o2, _, _ = _run(mea, seg, "bf16", causal=True, slopes=slopes)
+        assert np.array_equal(host_bits(o2), got[:, a:b]), f"segment {s}"
+
+
+def test_gqa_equals_repeated_kv_bitwise(mea):
+    c = inp.dense_case(32, 2, 200, 200, 8, 2, 64, "fp16")
+    rep = dict(c, k=np.repeat(c["k"], 4, axis=2), v=np.repeat(c["v"], 4, axis=2))
+    for causal in (False, True):
+        o1, _, _ = _run(mea, c, "fp16", causal=causal)
+        o2, _, _ = _run(mea, rep, "fp16", causal=causal)
+        assert np.array_equal(host_bits(o1), host_bits(o2)), causal
+
+
+def test_first_causal_row_is_v0_bitwise(mea):
+    c = inp.dense_case(33, 2, 130, 130, 4, 2, 128, "bf16")
+    out, _, _ = _run(mea, c, "bf16", causal=True, slopes=inp.alibi_slopes(4))
+    got = host_bits(out)
+    for h in range(4):
+        assert np.array_equal(got[:, 0, h], c["v"][:, 0, h // 2])
+
+
+def test_rows_sum_to_one(mea):
+    """V = 1: every output is 1 up to the rounding of P to bf16 before P.V."""
+    c = inp.dense_case(34, 2, 300, 300, 4, 4, 64, "bf16")
+    c["v"] = inp.round_bits(np.ones(c["v"].shape, np.float32), "bf16")
+    for causal in (False, True):
+        out, _, _ = _run(mea, c, "bf16", causal=causal, slopes=inp.alibi_slopes(4))
+        assert report(f"ones causal={causal}", host_f64(out), np.ones(out.shape), TOL["bf16"]) <= TOL["bf16"]
+
+
+def test_deterministic(mea):
+    c = inp.dense_case(35, 2, 1024, 1024, 8, 8, 128, "bf16")
+    o1, _, _ = _run(mea, c, "bf16", causal=True)
+    for _ in range(3):
+        o2, _, _ = _run(mea, c, "bf16", causal=True)
+        assert torch.equal(o1, o2)
+
+
+def test_no_nan_from_neighbours(mea):
+    """Packed rows beyond the last segment end are never read: NaN there
+    (inside the buffer) does not reach the output."""
+    lengths = [100, 60]
+    c = inp.varlen_case(36, lengths, 2, 2, 64, "bf16")
+    T = int(c["seqstart"][-1])
+    pad = 50
+    for key in ("q", "k", "v"):
+        x = np.full((1, T + pad) + c[key].shape[2:], inp.POISON["bf16"], np.uint16)
+        x[:, :T] = c[key]
+        c[key] = x
+    st = np.append(c["seqstart"], T + pad).astype(np.int32)   # a third segment of NaN rows
+    q, k, v = dev(c["q"], "bf16"), dev(c["k"], "bf16"), dev(c["v"], "bf16")
+    out = mea.fwd(q, k, v, causal=True, seqstart_q=i32(st))
+    torch.cuda.synchronize()
+    got = host_f64(out)[0, :T]
+    assert np.all(np.isfinite(got))
+    want, _ = orc.fwd(c["q"][:, :T], c["k"][:, :T], c["v"][:, :T], "bf16", 0.125, causal=True,
+                      seqstart_q=st[:3])
+    assert report("nan neighbours", got, want[0], TOL["bf16"]) <= TOL["bf16"]
