@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM:
+
+  1. forward, B=4, M=N=4096, H=16, D=64, bf16, no mask   (the headline)
+  2. forward, same shapes, causal mask
+  3. forward, 8 packed segments (lengths uniform in [64, 2048]), Hq=32,
+     Hkv=8, D=128, bf16, block-diagonal causal mask + ALiBi
+  4. decode step, B=32, contexts uniform in [1024, 32768], Hq=32, Hkv=8,
+     D=128, bf16 KV cache of 32768 slots per sequence
+
+Prints ONE JSON line on stdout. ``value`` is the headline forward throughput
+(algorithmic TFLOP/s of item 1: 4*B*H*M*N*D flops over its average launch
+time, measured with HIP events on the stream the kernel runs on); the other
+items are reported beside it, decode as algorithmic HBM GB/s (K and V bytes
+of every sequence's context plus q and out). Progress goes to stderr.
+
+``cpu_baseline`` times the fp64 oracle (test infrastructure) on the host's
+cores over a bounded sample of item 1 (rows of the first batch row, all
+heads, until about --cpu-seconds have passed); ``cpu_baseline_decode`` does
+the same for item 4 (whole sequences).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def build_inputs(torch, inp):
+    t0 = time.time()
+    x = {}
+    c = inp.dense_case(3, 4, 4096, 4096, 16, 16, 64, "bf16")
+    x["dense"] = {k: to_dev(c[k], torch) for k in ("q", "k", "v")}
+    x["dense_host"] = c
+    lengths = inp.segment_lengths(4, 8, 64, 2048)
+    v = inp.varlen_case(4, lengths, 32, 8, 128, "bf16")
+    x["varlen"] = {k: to_dev(v[k], torch) for k in ("q", "k", "v")}
+    x["varlen"]["seqstart"] = torch.from_numpy(v["seqstart"]).cuda()
+    x["varlen"]["slopes"] = torch.from_numpy(inp.alibi_slopes(32)).cuda()
+    x["lengths"] = lengths
+    log(f"[bench] forward inputs ready ({time.time() - t0:.1f}s); packed lengths {lengths.tolist()}")
+
+    B, S, Hq, Hkv, D = 32, 32768, 32, 8, 128
+    ctx = inp.context_lengths(5, B, 1024, 32768)
+    kc = torch.empty((B, S, Hkv, D), dtype=torch.int16, device="cuda")
+    vc = torch.empty_like(kc)
+    poison = int(np.uint16(inp.POISON["bf16"]).view(np.int16))
+    kc.fill_(poison)
+    vc.fill_(poison)
+
+    def rows(b):
+        return b, inp.decode_cache_rows(5, b, int(ctx[b]), Hkv, D, "bf16")
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        for b, (kb, vb) in ex.map(rows, range(B)):
+            kc[b, :ctx[b]] = torch.from_numpy(kb.view(np.int16)).cuda()
+            vc[b, :ctx[b]] = torch.from_numpy(vb.view(np.int16)).cuda()
+    x["decode"] = {
+        "q": to_dev(inp.normal_bits(5, (B, Hq, D), "bf16", 0), torch),
+        "kc": kc.view(torch.bfloat16), "vc": vc.view(torch.bfloat16),
+        "ctx": torch.from_numpy(ctx).cuda(), "ctx_host": ctx,
+    }
+    log(f"[bench] decode cache ready ({time.time() - t0:.1f}s); sum(ctx)={int(ctx.sum())}")
+    return x
+
+
+def cpu_baseline_fwd(c, seconds):
+    """fp64 oracle over blocks of 512 query rows (all 16 heads, all 4096 keys),
+    batch row by batch row, until about ``seconds`` have passed or the whole
+    workload is done."""
+    import oracle.attention as orc
+    from threadpoolctl import threadpool_info
+    rows_done, t0 = 0, time.time()
+    scale = float(np.float32(1.0 / 8.0))
+    while rows_done < 4 * 4096 and time.time() - t0 < seconds:
+        b, r0 = divmod(rows_done, 4096)
+        orc.fwd_rows(c["q"], c["k"], c["v"], "bf16", scale, b, np.arange(r0, r0 + 512))
+        rows_done += 512
+    dt = time.time() - t0
+    flops = 4.0 * 16 * rows_done * 4096 * 64
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} of 16384 query rows (batch-major) x 16 heads x 4096 keys, no mask, "
+                      f"{flops / 1e9:.2f} GFLOP in {dt:.1f} s"}
+
+
+def cpu_baseline_decode(ctx, seconds):
+    """fp64 oracle decode of whole sequences (all 32 heads) until the time is up."""
+    import mea_inputs as inp
+    import oracle.attention as orc
+    from threadpoolctl import threadpool_info
+    B, Hq, Hkv, D = 32, 32, 8, 128
+    q = inp.normal_bits(5, (B, Hq, D), "bf16", 0)
+    done, nbytes, busy = [], 0, 0.0
+    for b in range(B):
+        kb, vb = inp.decode_cache_rows(5, b, int(ctx[b]), Hkv, D, "bf16")
+        t0 = time.time()
+        orc.decode(q[b:b + 1], kb[None], vb[None], ctx[b:b + 1], "bf16", float(np.float32(1 / np.sqrt(D))))
+        busy += time.time() - t0
+        done.append(b)
+        nbytes += int(ctx[b]) * Hkv * D * 2 * 2 + Hq * D * 2 * 2
+        if busy >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": nbytes / busy / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} whole sequences (ctx {[int(ctx[b]) for b in done]}), "
+                      f"{nbytes / 1e9:.3f} GB of K/V in {busy:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mea_inputs as inp
+    import memory_efficient_exact_tiled_amd as mea
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    x = build_inputs(torch, inp)
+    d, vl, dc = x["dense"], x["varlen"], x["decode"]
+    ws = torch.empty(mea.decode_workspace_bytes(32, 32, 128, 32768), dtype=torch.uint8, device="cuda")
+    out_d = torch.empty_like(d["q"])
+    out_c = torch.empty_like(d["q"])
+    out_v = torch.empty_like(vl["q"])
+    out_dec = torch.empty_like(dc["q"])
+
+    items = [
+        ("fwd_noncausal", lambda: mea.fwd(d["q"], d["k"], d["v"], out=out_d)),
+        ("fwd_causal", lambda: mea.fwd(d["q"], d["k"], d["v"], causal=True, out=out_c)),
+        ("fwd_varlen", lambda: mea.fwd(vl["q"], vl["k"], vl["v"], causal=True, seqstart_q=vl["seqstart"],
+                                       alibi_slopes=vl["slopes"], out=out_v)),
+        ("decode", lambda: mea.decode(dc["q"], dc["kc"], dc["vc"], dc["ctx"], out=out_dec, workspace=ws)),
+    ]
+    events = {name: [] for name, _ in items}
+
+    def step(record):
+        for name, fn in items:
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events[name].append((e0, e1))
+            else:
+                fn()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {wall:.3f}s")
+
+    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev])) for n, ev in events.items()}
+    L = x["lengths"].astype(np.int64)
+    flops = {
+        "fwd_noncausal": 4.0 * 4 * 16 * 4096 * 4096 * 64,
+        "fwd_causal": 4.0 * 4 * 16 * 64 * (4096 * 4097 / 2),
+        "fwd_varlen": 4.0 * 128 * 32 * float(np.sum(L * (L + 1) // 2)),
+    }
+    ctx = x["decode"]["ctx_host"].astype(np.int64)
+    dec_bytes = float(ctx.sum() * 8 * 128 * 2 * 2 + 32 * 32 * 128 * 2 * 2)
+    tflops = {n: flops[n] / (ms[n] * 1e-3) / 1e12 for n in flops}
+    dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
+    for n in flops:
+        log(f"[bench] {n}: {ms[n] * 1e3:.1f} us  {tflops[n]:.1f} TFLOP/s ({tflops[n] / PEAK_MFMA_TFLOPS:.1%} of peak)")
+    log(f"[bench] decode: {ms['decode'] * 1e3:.1f} us  {dec_gbs:.1f} GB/s ({dec_gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
+
+    res = {
+        "metric": "attn fwd TFLOP/s (bf16, M=4096, % MFMA peak); decode HBM GB/s",
+        "value": round(tflops["fwd_noncausal"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "attention forward B=4 M=N=4096 H=16 D=64 bf16 (no mask; causal beside it) "
+                        "+ packed 8x[64,2048] Hq=32 Hkv=8 D=128 block-diag causal ALiBi "
+                        "+ decode B=32 ctx[1024,32768] Hq=32 Hkv=8 D=128",
+            "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops["fwd_noncausal"], 2), "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops["fwd_noncausal"] / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+            "kernel": "fwd_kernel<bf16,64>", "avg_launch_us": round(ms["fwd_noncausal"] * 1e3, 2),
+        },
+        "roofline_decode": {
+            "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
+            "avg_launch_us": round(ms["decode"] * 1e3, 2),
+        },
+        "per_item": {n: {"avg_launch_us": round(ms[n] * 1e3, 2),
+                         **({"tflops": round(tflops[n], 2), "frac_mfma_peak": round(tflops[n] / PEAK_MFMA_TFLOPS, 4)}
+                            if n in tflops else
+                            {"gbs": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)})}
+                     for n in ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host (bounded sample)")
+        res["cpu_baseline"] = cpu_baseline_fwd(x["dense_host"], args.cpu_seconds)
+        res["cpu_baseline_decode"] = cpu_baseline_decode(x["decode"]["ctx_host"], args.cpu_seconds / 2)
+        log(f"[bench] cpu baseline: {res['cpu_baseline']}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
