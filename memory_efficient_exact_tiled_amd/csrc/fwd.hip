@@ -45,7 +45,10 @@ constexpr int kBN = 64;
 
 template <int D>
 struct FwdShape {
-  static constexpr int QB = 2;                  // 32-row query blocks per wave
+  // 32-row query blocks per wave: two at D=64, one at D=128, so that a wave
+  // fits in 256 registers and two waves share each SIMD (one computes the
+  // softmax while the other keeps the matrix core busy).
+  static constexpr int QB = D == 64 ? 2 : 1;
   static constexpr int QW = 32 * QB;            // query rows per wave
   static constexpr int BM = kWaves * QW;        // query rows per work-group
   static constexpr int LDS = D + 16;            // padded LDS row stride (elements)
@@ -55,7 +58,7 @@ struct FwdShape {
 };
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) fwd_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel(const FwdParams p) {
   using S = FwdShape<D>;
   using MF = Mfma<T>;
   typedef typename MF::v8 v8;
