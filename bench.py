@@ -136,6 +136,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode",
+                    help="comma-separated subset of the step to run (for profiling one kernel)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy, 5 times (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -149,6 +153,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30,
+                          "launches": 5}), flush=True)
+        return
     x = build_inputs(torch, inp)
     d, vl, dc = x["dense"], x["varlen"], x["decode"]
     ws = torch.empty(mea.decode_workspace_bytes(32, 32, 128, 32768), dtype=torch.uint8, device="cuda")
@@ -164,6 +178,12 @@ def main():
                                        alibi_slopes=vl["slopes"], out=out_v)),
         ("decode", lambda: mea.decode(dc["q"], dc["kc"], dc["vc"], dc["ctx"], out=out_dec, workspace=ws)),
     ]
+    wanted = set(args.items.split(","))
+    unknown = wanted - {n for n, _ in items}
+    if unknown:
+        print(f"unknown items {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    items = [(n, fn) for n, fn in items if n in wanted]
     events = {name: [] for name, _ in items}
 
     def step(record):
@@ -190,22 +210,31 @@ def main():
 
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev])) for n, ev in events.items()}
     L = x["lengths"].astype(np.int64)
-    flops = {
+    flops_all = {
         "fwd_noncausal": 4.0 * 4 * 16 * 4096 * 4096 * 64,
         "fwd_causal": 4.0 * 4 * 16 * 64 * (4096 * 4097 / 2),
         "fwd_varlen": 4.0 * 128 * 32 * float(np.sum(L * (L + 1) // 2)),
     }
     ctx = x["decode"]["ctx_host"].astype(np.int64)
     dec_bytes = float(ctx.sum() * 8 * 128 * 2 * 2 + 32 * 32 * 128 * 2 * 2)
-    tflops = {n: flops[n] / (ms[n] * 1e-3) / 1e12 for n in flops}
-    dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
-    for n in flops:
-        log(f"[bench] {n}: {ms[n] * 1e3:.1f} us  {tflops[n]:.1f} TFLOP/s ({tflops[n] / PEAK_MFMA_TFLOPS:.1%} of peak)")
-    log(f"[bench] decode: {ms['decode'] * 1e3:.1f} us  {dec_gbs:.1f} GB/s ({dec_gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
+    tflops = {n: flops_all[n] / (ms[n] * 1e-3) / 1e12 for n in flops_all if n in ms}
+    dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9 if "decode" in ms else None
+    per_item = {}
+    for n in ms:
+        if n in tflops:
+            log(f"[bench] {n}: {ms[n] * 1e3:.1f} us  {tflops[n]:.1f} TFLOP/s "
+                f"({tflops[n] / PEAK_MFMA_TFLOPS:.1%} of peak)")
+            per_item[n] = {"avg_launch_us": round(ms[n] * 1e3, 2), "tflops": round(tflops[n], 2),
+                           "frac_mfma_peak": round(tflops[n] / PEAK_MFMA_TFLOPS, 4)}
+        else:
+            log(f"[bench] decode: {ms[n] * 1e3:.1f} us  {dec_gbs:.1f} GB/s ({dec_gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
+            per_item[n] = {"avg_launch_us": round(ms[n] * 1e3, 2), "gbs": round(dec_gbs, 1),
+                           "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dec_bytes}
+    head = tflops.get("fwd_noncausal")
 
     res = {
         "metric": "attn fwd TFLOP/s (bf16, M=4096, % MFMA peak); decode HBM GB/s",
-        "value": round(tflops["fwd_noncausal"], 2),
+        "value": round(head, 2) if head is not None else None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -220,24 +249,22 @@ def main():
             "workload": "attention forward B=4 M=N=4096 H=16 D=64 bf16 (no mask; causal beside it) "
                         "+ packed 8x[64,2048] Hq=32 Hkv=8 D=128 block-diag causal ALiBi "
                         "+ decode B=32 ctx[1024,32768] Hq=32 Hkv=8 D=128",
+            "items": sorted(ms),
             "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)",
         },
-        "roofline": {
-            "bound": "mfma", "achieved": round(tflops["fwd_noncausal"], 2), "peak": PEAK_MFMA_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops["fwd_noncausal"] / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+        "roofline": None if head is None else {
+            "bound": "mfma", "achieved": round(head, 2), "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(head / PEAK_MFMA_TFLOPS, 4), "traffic": None,
             "kernel": "fwd_kernel<bf16,64>", "avg_launch_us": round(ms["fwd_noncausal"] * 1e3, 2),
+            "algorithmic_flops": flops_all["fwd_noncausal"],
         },
-        "roofline_decode": {
+        "roofline_decode": None if dec_gbs is None else {
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
             "kernel": "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
-            "avg_launch_us": round(ms["decode"] * 1e3, 2),
+            "avg_launch_us": round(ms["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes,
         },
-        "per_item": {n: {"avg_launch_us": round(ms[n] * 1e3, 2),
-                         **({"tflops": round(tflops[n], 2), "frac_mfma_peak": round(tflops[n] / PEAK_MFMA_TFLOPS, 4)}
-                            if n in tflops else
-                            {"gbs": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)})}
-                     for n in ms},
+        "per_item": per_item,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

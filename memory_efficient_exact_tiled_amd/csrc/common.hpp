@@ -8,6 +8,7 @@
 //   v_mfma_f32_16x16x32_{bf16,f16}: A lane l holds row l%16, k = (l/16)*8 + 0..7;
 //     B lane l holds column l%16, same k; C/D lane l holds column l%16 and rows
 //     (l/16)*4 + r for r = 0..3.
+//   v_mfma_f32_16x16x16{bf16_1k,f16}: as above with k = (l/16)*4 + 0..3.
 //   ds_read_b64_tr_b16: within each group of 16 lanes, lane s addresses 8 bytes
 //     (4 elements); lane s of the result receives element (s % 4) of the
 //     addresses given by lanes 4*j + s/4, j = 0..3, i.e. when the 16 lanes
@@ -42,6 +43,10 @@ struct Mfma<__bf16> {
   static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mma16k16(v4 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
+                                                     c, 0, 0, 0);
+  }
 };
 
 template <>
@@ -53,6 +58,9 @@ struct Mfma<_Float16> {
   }
   static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16k16(v4 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
 };
 
@@ -68,6 +76,11 @@ __device__ __forceinline__ typename Mfma<T>::v8 lds_tr_x8(const uint16_t* p0, co
 }
 
 template <typename T>
+__device__ __forceinline__ typename Mfma<T>::v4 lds_tr_x4(const uint16_t* p0) {
+  return __builtin_bit_cast(typename Mfma<T>::v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0)));
+}
+
+template <typename T>
 __device__ __forceinline__ typename Mfma<T>::v8 load_v8(const uint16_t* p) {
   return __builtin_bit_cast(typename Mfma<T>::v8, *reinterpret_cast<const uint4*>(p));
 }
@@ -75,6 +88,25 @@ __device__ __forceinline__ typename Mfma<T>::v8 load_v8(const uint16_t* p) {
 template <typename T>
 __device__ __forceinline__ typename Mfma<T>::v8 zero_v8() {
   return __builtin_bit_cast(typename Mfma<T>::v8, make_uint4(0u, 0u, 0u, 0u));
+}
+
+// Raw buffer resource over [base, base + bytes): 16-byte loads at offsets at
+// or past `bytes` return zeros instead of touching memory, which is how row
+// ranges (segment ends, context lengths) are enforced without branches.
+// Word 3 is the gfx9-family default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Byte count of rows [0, n) of a row-major tensor, clamped to the 32-bit
+// range of a buffer resource (n <= 0 gives 0).
+__device__ __forceinline__ uint32_t rows_bytes(long long n, long long row_bytes) {
+  const long long b = n > 0 ? n * row_bytes : 0;
+  return b > 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
 }
 
 // 2^x on the transcendental unit (v_exp_f32): exact 0 for -inf.

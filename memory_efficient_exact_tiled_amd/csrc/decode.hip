@@ -8,21 +8,26 @@
 // goal is to keep enough loads in flight and to read each K/V row once for
 // all query heads that share it.
 //
-// decode_split: one work-group per (sequence b, KV head g, block of up to 16
-//   of g's query heads, chunk of kDecodeChunk keys); chunks at or past ctx
-//   exit at once. Its 4 waves split the chunk; each wave walks 32 keys per
-//   step:
+// decode_split: one wave per (sequence b, KV head g, block of up to 16 of g's
+//   query heads, chunk of kDecodeChunk keys); the 8 waves of a work-group take
+//   8 consecutive (g, block) units of the same chunk, so they read the same
+//   cache rows (all KV heads of a position sit side by side) at the same
+//   time. Chunks at or past ctx exit at once. A wave walks its chunk 16 keys
+//   per step with two register stages (the next step's loads are in flight
+//   while the current one is computed):
 //     * K rows are loaded from HBM straight into the A-operand layout of
 //       v_mfma_f32_16x16x32 (row = key, k = head dim), the query heads of the
 //       group form the B operand (one column per head), so S^T = K Q^T reads
 //       each key once for all heads of the group;
 //     * the online softmax runs per head (one head per lane column);
-//     * V rows go HBM -> LDS (a per-wave region) and come back transposed
-//       through ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T;
-//     * slots at or past ctx are never loaded (zero-filled), so whatever the
-//       cache holds there (NaN included) cannot reach the result.
-//   The 4 wave partials are merged in LDS and the work-group writes one
-//   partial (row max m in log2 units, row sum l, unnormalised O) per head.
+//     * V rows go HBM -> registers -> the wave's LDS region and come back
+//       transposed through ds_read_b64_tr_b16 as the A operand of
+//       O^T = V^T P^T (v_mfma_f32_16x16x16);
+//     * all K/V loads are buffer loads whose resource ends at the chunk's
+//       last key: slots at or past ctx read as zeros and are masked, so
+//       whatever the cache holds there (NaN included) cannot reach the result.
+//   Each wave writes its partial (row max m in log2 units, row sum l,
+//   unnormalised O) per head to the workspace.
 // decode_combine: per (b, query head) merges the partials of all chunks by
 //   their maxima: O = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c, which
 //   is the block update of the online softmax ("FlashAttention (2022)",
@@ -34,44 +39,51 @@ namespace mea {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kStep = 32;                          // keys per wave step
-constexpr int kWaveKeys = kDecodeChunk / kWaves;   // keys per wave per chunk
+constexpr int kWaves = 8;      // (KV head, head block) units per work-group
+constexpr int kKStep = 16;     // keys per wave step
+constexpr int kStages = 2;     // register stages of K/V per wave
 
-template <int D>
+template <int D, int KSTEP>
 struct DecShape {
   static constexpr int LDS = D + 16;               // padded row stride of a V block (elements)
-  static constexpr int VTILE = kStep * LDS;        // elements per wave's V block
+  static constexpr int VTILE = KSTEP * LDS;        // elements per wave's V block
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
-  static constexpr int NLD = kStep * CPR / 64;     // chunks per lane per step
-  static constexpr int SMEM_BYTES = kWaves * VTILE * 2;
-  static constexpr int MERGE_BYTES = (2 * kWaves * 16 + kWaves * 16 * D) * 4;
-  static_assert(MERGE_BYTES <= SMEM_BYTES, "merge buffer must fit in the V region");
+  static constexpr int NLD = KSTEP * CPR / 64;     // V chunks per lane per step
 };
 
-template <typename T, int D>
-__global__ void __launch_bounds__(256) decode_split_kernel(const DecParams p) {
-  using S = DecShape<D>;
+// One wave = one (KV head g, block of up to 16 of g's query heads) over one
+// chunk of keys; the waves of a work-group take consecutive units, so they
+// read the same cache rows at the same time. KSTEP keys per step (16 or 32);
+// STAGES register stages of K/V: the loads of the next STAGES-1 steps are in
+// flight while the current step is computed.
+template <typename T, int D, int KSTEP, int STAGES>
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_split_kernel(const DecParams p) {
+  using S = DecShape<D, KSTEP>;
   using MF = Mfma<T>;
   typedef typename MF::v8 v8;
+  typedef typename MF::v4 v4;
   constexpr int LDS = S::LDS, VTILE = S::VTILE, CPR = S::CPR, NLD = S::NLD;
   constexpr int DS = D / 32;     // k-steps of the score product (16x16x32)
   constexpr int DB = D / 16;     // 16-row output blocks
+  constexpr int KB = KSTEP / 16; // 16-key blocks per step
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM_BYTES / 2];
-
-  const int chunk = blockIdx.x;
-  const int g = blockIdx.y / p.nhb;
-  const int hb = blockIdx.y - g * p.nhb;
-  const int b = blockIdx.z;
-  const int ctx = min(max(p.ctx[b], 0), p.S_max);
-  const int start = chunk * kDecodeChunk;
-  if (start >= ctx) return;
-  const int end = min(start + kDecodeChunk, ctx);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * VTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int chunk = blockIdx.x;
+  const int unit = blockIdx.y * kWaves + wave;
+  const int b = blockIdx.z;
+  if (unit >= p.Hkv * p.nhb) return;
+  const int g = unit / p.nhb;
+  const int hb = unit - g * p.nhb;
+  const int ctx = min(max(p.ctx[b], 0), p.S_max);
+  const int w0 = chunk * kDecodeChunk;
+  if (w0 >= ctx) return;
+  const int w1 = min(w0 + kDecodeChunk, ctx);
+
   const int col = lane & 15;     // query head within the block (MFMA column)
   const int grp = lane >> 4;
   const int nh = min(16, p.group - hb * 16);
@@ -91,9 +103,6 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecParams p) {
   const uint16_t* vbase = p.vc + (long long)b * p.S_max * rstride + (long long)g * D;
   uint16_t* Vw = smem + wave * VTILE;
 
-  const int w0 = start + wave * kWaveKeys;
-  const int w1 = min(w0 + kWaveKeys, end);
-
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[DB];
 #pragma unroll
@@ -105,40 +114,48 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecParams p) {
   const int vrow = grp * 4 + (ll >> 2);
   const int vcol = 4 * (ll & 3);
 
-  for (int key0 = w0; key0 < w1; key0 += kStep) {
-    // K in the A-operand layout, V rows staged for LDS.
-    v8 kf[2][DS];
+  struct Stage {
+    v8 kf[KB][DS];    // K, A-operand layout (row = key, k = head dim)
+    uint4 vst[NLD];   // V rows, bound for LDS
+  };
+  // Per-lane byte offsets inside one step's rows; the buffer resource is
+  // rebased on each step and ends at the chunk's last key, so rows past it
+  // read as zeros.
+  const uint32_t row_bytes = (uint32_t)rstride * 2u;
+  const uint32_t koff_lane = (uint32_t)col * row_bytes + (uint32_t)grp * 16u;
+  uint32_t voff_lane[NLD];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = key0 + kb * 16 + col;
+  for (int i = 0; i < NLD; ++i) {
+    const int ch = lane + i * 64;
+    const int r = ch / CPR;
+    voff_lane[i] = (uint32_t)r * row_bytes + (uint32_t)(ch - r * CPR) * 16u;
+  }
+  auto load = [&](Stage& sg, int key0) {
+    const uint32_t bytes = rows_bytes(w1 - key0, row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (long long)key0 * rstride, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (long long)key0 * rstride, bytes);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int st = 0; st < DS; ++st)
-        kf[kb][st] = key < w1 ? load_v8<T>(kbase + (long long)key * rstride + st * 32 + grp * 8) : zero_v8<T>();
-    }
-    uint4 vst[NLD];
+        sg.kf[kb][st] = __builtin_bit_cast(v8, buf_load16(rk, koff_lane + kb * 16 * row_bytes + st * 64));
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int ch = lane + i * 64;
-      const int r = ch / CPR;
-      const int cc = (ch - r * CPR) * 8;
-      const int key = key0 + r;
-      vst[i] = key < w1 ? *reinterpret_cast<const uint4*>(vbase + (long long)key * rstride + cc)
-                        : make_uint4(0u, 0u, 0u, 0u);
-    }
-
-    f32x4 s[2];
+    for (int i = 0; i < NLD; ++i) sg.vst[i] = buf_load16(rv, voff_lane[i]);
+  };
+  auto compute = [&](const Stage& sg, int key0) {
+    f32x4 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int st = 0; st < DS; ++st) s[kb] = MF::mma16(kf[kb][st], qf[st], s[kb]);
+      for (int st = 0; st < DS; ++st) s[kb] = MF::mma16(sg.kf[kb][st], qf[st], s[kb]);
     }
 
-    // Scores in log2 units; keys past the wave's range are masked.
+    // Scores in log2 units; keys past the chunk are masked.
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = key0 + kb * 16 + grp * 4 + r;
@@ -161,109 +178,171 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecParams p) {
       m_run = mn;
     }
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    v8 pf;
+    T pv[KB * 4];
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pv = fast_exp2(s[kb][r] - mu);
-        psum += pv;
-        pf[kb * 4 + r] = (T)pv;
+        const float e = fast_exp2(s[kb][r] - mu);
+        psum += e;
+        pv[kb * 4 + r] = (T)e;
       }
     l_run += psum;
 
     // V block -> this wave's LDS region, then O^T += V^T P^T. LDS operations
     // of one wave complete in order; the compiler barriers keep the program
     // order of stores and transpose reads.
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int ch = lane + i * 64;
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(Vw + r * LDS + cc) = vst[i];
+      *reinterpret_cast<uint4*>(Vw + r * LDS + cc) = sg.vst[i];
     }
     __asm__ volatile("" ::: "memory");
+    if constexpr (KSTEP == 32) {
+      v8 pf;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint16_t* a0 = Vw + vrow * LDS + db * 16 + vcol;
-      const v8 vf = lds_tr_x8<T>(a0, a0 + 16 * LDS);
-      o[db] = MF::mma16(vf, pf, o[db]);
+      for (int u = 0; u < 8; ++u) pf[u] = pv[u];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* a0 = Vw + vrow * LDS + db * 16 + vcol;
+        o[db] = MF::mma16(lds_tr_x8<T>(a0, a0 + 16 * LDS), pf, o[db]);
+      }
+    } else {
+      v4 pf;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pf[u] = pv[u];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = MF::mma16k16(lds_tr_x4<T>(Vw + vrow * LDS + db * 16 + vcol), pf, o[db]);
     }
     __asm__ volatile("" ::: "memory");
+  };
+
+  if constexpr (STAGES == 3) {
+    Stage s0, s1, s2;
+    int key0 = w0;
+    load(s0, key0);
+    if (key0 + KSTEP < w1) load(s1, key0 + KSTEP);
+    while (true) {
+      if (key0 + 2 * KSTEP < w1) load(s2, key0 + 2 * KSTEP);
+      compute(s0, key0);
+      key0 += KSTEP;
+      if (key0 >= w1) break;
+      if (key0 + 2 * KSTEP < w1) load(s0, key0 + 2 * KSTEP);
+      compute(s1, key0);
+      key0 += KSTEP;
+      if (key0 >= w1) break;
+      if (key0 + 2 * KSTEP < w1) load(s1, key0 + 2 * KSTEP);
+      compute(s2, key0);
+      key0 += KSTEP;
+      if (key0 >= w1) break;
+    }
+  } else if constexpr (STAGES == 2) {
+    Stage sa, sb;
+    int key0 = w0;
+    load(sa, key0);
+    while (true) {
+      if (key0 + KSTEP < w1) load(sb, key0 + KSTEP);
+      compute(sa, key0);
+      key0 += KSTEP;
+      if (key0 >= w1) break;
+      if (key0 + KSTEP < w1) load(sa, key0 + KSTEP);
+      compute(sb, key0);
+      key0 += KSTEP;
+      if (key0 >= w1) break;
+    }
+  } else {
+    for (int key0 = w0; key0 < w1; key0 += KSTEP) {
+      Stage sg;
+      load(sg, key0);
+      compute(sg, key0);
+    }
   }
 
-  // ---- merge the 4 wave partials, write the chunk partial ------------------
+  // ---- this wave's partial for the chunk ------------------------------------
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  __syncthreads();
-  float* wm = reinterpret_cast<float*>(smem);
-  float* wl = wm + kWaves * 16;
-  float* wo = wl + kWaves * 16;
-  if (grp == 0) {
-    wm[wave * 16 + col] = m_run;
-    wl[wave * 16 + col] = l_tot;
-  }
+  if (real) {
+    const long long slot = ((long long)b * p.Hq + h) * p.nchunk + chunk;
+    float* dst = p.ws_o + slot * D + grp * 4;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wo[(wave * 16 + col) * D + db * 16 + grp * 4 + r] = o[db][r];
-  __syncthreads();
-
-  for (int idx = tid; idx < nh * D; idx += kWaves * 64) {
-    const int hc = idx / D;
-    const int d = idx - hc * D;
-    float mstar = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, wm[w * 16 + hc]);
-    const float mref = mstar == -INFINITY ? 0.f : mstar;
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = fast_exp2(wm[w * 16 + hc] - mref);
-      acc += e * wo[(w * 16 + hc) * D + d];
-      lsum += e * wl[w * 16 + hc];
-    }
-    const int hh = g * p.group + hb * 16 + hc;
-    const long long slot = ((long long)b * p.Hq + hh) * p.nchunk + chunk;
-    p.ws_o[slot * D + d] = acc;
-    if (d == 0) {
-      p.ws_ml[slot * 2 + 0] = mstar;
-      p.ws_ml[slot * 2 + 1] = lsum;
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16) = o[db];
+    if (grp == 0) {
+      p.ws_ml[slot * 2 + 0] = m_run;
+      p.ws_ml[slot * 2 + 1] = l_tot;
     }
   }
 }
 
+// One work-group of 256 threads per (sequence, query head). Thread t reads
+// column d = t % D of the partial outputs of chunks c = t / D, t / D + 256 / D,
+// ... so every chunk's row is one coalesced read, and the 256 / D column
+// groups are summed through LDS at the end.
 template <typename T, int D>
-__global__ void __launch_bounds__(D) decode_combine_kernel(const DecParams p) {
+__global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) {
+  constexpr int NT = 256, CG = NT / D;
+  __shared__ float red[NT];
+  __shared__ float wmax[NT / 64];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int ctx = min(max(p.ctx[b], 0), p.S_max);
   const int n = (ctx + kDecodeChunk - 1) / kDecodeChunk;
   const long long base = ((long long)b * p.Hq + h) * p.nchunk;
-  float mstar = -INFINITY;
-  for (int i = 0; i < n; ++i) mstar = fmaxf(mstar, p.ws_ml[(base + i) * 2]);
+
+  float m = -INFINITY;
+  for (int i = tid; i < n; i += NT) m = fmaxf(m, p.ws_ml[(base + i) * 2]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  float mstar = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) mstar = fmaxf(mstar, wmax[w]);
   const float mref = mstar == -INFINITY ? 0.f : mstar;
+
+  const int d = tid % D;
+  const int cg = tid / D;
   float acc = 0.f, lsum = 0.f;
-  for (int i = 0; i < n; ++i) {
+#pragma unroll 4
+  for (int i = cg; i < n; i += CG) {
     const float e = fast_exp2(p.ws_ml[(base + i) * 2] - mref);
     acc += e * p.ws_o[(base + i) * D + d];
     lsum += e * p.ws_ml[(base + i) * 2 + 1];
   }
-  // A row with no keys has lsum == 0 and returns 0; NaN inputs stay NaN.
-  const float r = lsum != 0.f ? acc / lsum : 0.f;
-  const T w = (T)r;
-  p.out[((long long)b * p.Hq + h) * D + d] = __builtin_bit_cast(uint16_t, w);
+  red[tid] = acc;
+  __syncthreads();
+  if (cg == 0) {
+#pragma unroll
+    for (int g = 1; g < CG; ++g) acc += red[g * D + d];
+  }
+  __syncthreads();
+  red[tid] = lsum;
+  __syncthreads();
+  if (cg == 0) {
+#pragma unroll
+    for (int g = 1; g < CG; ++g) lsum += red[g * D + d];
+    // A row with no keys has lsum == 0 and returns 0; NaN inputs stay NaN.
+    const float r = lsum != 0.f ? acc / lsum : 0.f;
+    const T w = (T)r;
+    p.out[((long long)b * p.Hq + h) * D + d] = __builtin_bit_cast(uint16_t, w);
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(p.nchunk, p.Hkv * p.nhb, p.B), dim3(kWaves * 64), 0,
-                     stream, p);
+  const int units = p.Hkv * p.nhb;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages>),
+                     dim3(p.nchunk, (units + kWaves - 1) / kWaves, p.B), dim3(kWaves * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq, p.B), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq, p.B), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
