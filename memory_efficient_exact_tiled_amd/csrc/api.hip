@@ -93,7 +93,7 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M
   // offsets are 64-bit.
   const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
   if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
-  const int BM = mea::fwd_block_m(D);
+  const int BM = mea::fwd_block_m(D, causal);
 
   mea::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);

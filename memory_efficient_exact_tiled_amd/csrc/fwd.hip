@@ -10,16 +10,23 @@
 //
 // Work decomposition (one work-group = 4 waves = 256 threads):
 //   * a work-group owns BM = 4 * 32 * QB query rows of one (batch or packed
-//     segment, query head); wave w owns 32 * QB consecutive rows;
-//   * K/V blocks of BN = 64 keys are copied HBM -> registers -> LDS, double
-//     buffered so one barrier per block suffices; the next block's global
-//     loads are in flight while the current block is computed;
+//     segment, query head); wave w owns 32 * QB consecutive rows; two waves
+//     (three at QB=1, D=64) share each SIMD, so one wave's softmax overlaps
+//     another's matrix-core work; MFMA phases run at raised wave priority;
+//   * K/V blocks of BN = 64 keys are copied HBM -> registers -> LDS with
+//     buffer loads whose resource ends at the segment's last key (rows past
+//     it read as zeros), double buffered so one barrier per block suffices;
+//     the next block's loads are in flight while the current one is computed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
 //     registers for the whole kernel). With this orientation each lane holds
 //     one query's scores for 32 of the 64 keys, so the row max needs a single
-//     cross-lane step (lane l and l^32) and the row sum none until the end;
-//   * P^T is rounded to the input type in registers and fed straight back as
-//     the B operand of O^T = V^T P^T; V^T comes from the row-major V block
+//     cross-lane step (v_permlane32_swap between lanes l and l^32) and the
+//     row sum none until the end;
+//   * P^T is rounded to the input type in registers; the row sum is taken
+//     over those rounded values, two at a time with v_dot2_f32_{bf16,f16}
+//     (so the normaliser matches the weights P.V actually uses), and P^T is
+//     fed straight back as the B operand of O^T = V^T P^T; V^T comes from the
+//     row-major V block
 //     with ds_read_b64_tr_b16, which matches the key order P^T has in the
 //     score accumulators, so V is never transposed in memory;
 //   * causal and block-diagonal masks are index predicates evaluated only on
@@ -43,26 +50,35 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBN = 64;
 
-template <int D>
+// Query rows per wave = 32 * QB. Dense D=64 uses QB=2 (each K/V fragment read
+// from LDS feeds two query blocks); under a causal mask and at D=128 QB=1,
+// which halves the rows a diagonal block masks off and keeps a wave within
+// the register budget of several waves per SIMD.
+template <int D, int QB_>
 struct FwdShape {
-  // 32-row query blocks per wave: two at D=64, one at D=128, so that a wave
-  // fits in 256 registers and two waves share each SIMD (one computes the
-  // softmax while the other keeps the matrix core busy).
-  static constexpr int QB = D == 64 ? 2 : 1;
+  static constexpr int QB = QB_;
   static constexpr int QW = 32 * QB;            // query rows per wave
   static constexpr int BM = kWaves * QW;        // query rows per work-group
-  static constexpr int LDS = D + 16;            // padded LDS row stride (elements)
-  static constexpr int TILE = kBN * LDS;        // elements of one K or V block
+  // Padded LDS row strides (elements): K rows are read 16 rows x 16 bytes at
+  // a time (a stride of 4 banks mod 64 keeps those 16 rows on distinct
+  // banks), V rows 4 rows x 32 bytes at a time by the transpose read (a
+  // stride of 8 banks mod 64).
+  static constexpr int LDSK = D + 8;
+  static constexpr int LDS = D + 16;            // V
+  static constexpr int TILE = kBN * LDS;        // elements reserved per K or V block
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int NLD = kBN * CPR / (kWaves * 64);  // chunks per thread per tensor
+  // Waves per SIMD the register budget is tuned for.
+  static constexpr int WPE = (D == 64 && QB == 1) ? 3 : 2;
 };
 
-template <typename T, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel(const FwdParams p) {
-  using S = FwdShape<D>;
+template <typename T, int D, int QB_>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE))) fwd_kernel(const FwdParams p) {
+  using S = FwdShape<D, QB_>;
   using MF = Mfma<T>;
   typedef typename MF::v8 v8;
-  constexpr int QB = S::QB, QW = S::QW, BM = S::BM, LDS = S::LDS, TILE = S::TILE;
+  constexpr int QB = S::QB, QW = S::QW, BM = S::BM, LDS = S::LDS, LDSK = S::LDSK, TILE = S::TILE;
   constexpr int CPR = S::CPR, NLD = S::NLD;
   constexpr int DB = D / 32;   // 32-wide output column blocks
   constexpr int DS = D / 16;   // k-steps of the score product
@@ -158,21 +174,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // ---- K/V staging ---------------------------------------------------------
   uint4 kst[NLD], vst[NLD];
+  const uint32_t row_bytes = (uint32_t)p.kv_rstride * 2u;
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int ch = tid + i * (kWaves * 64);
+    const int r = ch / CPR;
+    ld_off[i] = (uint32_t)r * row_bytes + (uint32_t)(ch - r * CPR) * 16u;
+  }
   auto gload = [&](int kt) {
+    const uint32_t bytes = rows_bytes(N_s - kt * kBN, row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + koff + (long long)kt * kBN * p.kv_rstride, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + koff + (long long)kt * kBN * p.kv_rstride, bytes);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int ch = tid + i * (kWaves * 64);
-      const int r = ch / CPR;
-      const int cc = (ch - r * CPR) * 8;
-      const int key = kt * kBN + r;
-      if (key < N_s) {
-        const long long e = koff + (long long)key * p.kv_rstride + cc;
-        kst[i] = *reinterpret_cast<const uint4*>(p.k + e);
-        vst[i] = *reinterpret_cast<const uint4*>(p.v + e);
-      } else {
-        kst[i] = make_uint4(0u, 0u, 0u, 0u);
-        vst[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      kst[i] = buf_load16(rk, ld_off[i]);
+      vst[i] = buf_load16(rv, ld_off[i]);
     }
   };
   auto lstore = [&](int buf) {
@@ -182,7 +199,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int ch = tid + i * (kWaves * 64);
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(ks + r * LDS + cc) = kst[i];
+      *reinterpret_cast<uint4*>(ks + r * LDSK + cc) = kst[i];
       *reinterpret_cast<uint4*>(ks + TILE + r * LDS + cc) = vst[i];
     }
   };
@@ -213,15 +230,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        const v8 kf = load_v8<T>(Ks + (kb * 32 + l32) * LDS + st * 16 + hi * 8);
+        const v8 kf = load_v8<T>(Ks + (kb * 32 + l32) * LDSK + st * 16 + hi * 8);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = MF::mma32(kf, qf[qb][st], s[qb][kb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     const bool need_mask = (key_base + kBN > N_s) || (p.causal && key_base + kBN - 1 > wq0 + off);
     typename MF::v8 pf[QB][4];
@@ -251,7 +270,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      mx = wave_max_xor(mx, 32);
+      {
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+      }
       const float mt = mx * cc;
       if (__any(mt > m_run[qb] + kRescaleThreshold)) {
         const float mn = fmaxf(m_run[qb], mt);
@@ -264,23 +286,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         m_run[qb] = mn;
       }
       const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[qb][kb][r], cc, -mu));
-          s[qb][kb][r] = pv;
-          psum += pv;
-        }
-      l_run[qb] += psum;
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(fmaf(s[qb][kb][r], cc, -mu));
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int u = 0; u < 8; ++u) pf[qb][tt][u] = (T)s[qb][tt >> 1][(tt & 1) * 8 + u];
+      // Row sum of the rounded P (the values P.V uses), two at a time.
+      float psum = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        typedef T T2 __attribute__((ext_vector_type(2)));
+        const T2 one2 = {(T)1.f, (T)1.f};
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          const T2 pp = {pf[qb][tt][u], pf[qb][tt][u + 1]};
+          if constexpr (sizeof(T) == 2 && __is_same(T, __bf16))
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
+          else
+            psum = __builtin_amdgcn_fdot2(pp, one2, psum, false);
+        }
+      }
+      l_run[qb] += psum;
     }
 
     // O^T += V^T P^T
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -291,6 +324,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int qb = 0; qb < QB; ++qb) o[qb][db] = MF::mma32(vf, pf[qb][tt], o[qb][db]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- epilogue --------------------------------------------------------------
@@ -316,20 +350,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int QB>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
   const int grid = p.wg_per_xcd * 8;
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, QB>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
+  if (D == 64) return p.causal ? launch_typed<T, 64, 1>(p, stream) : launch_typed<T, 64, 2>(p, stream);
+  return launch_typed<T, 128, 1>(p, stream);
 }
 
 }  // namespace
 
-int fwd_block_m(int D) { return D == 64 ? FwdShape<64>::BM : FwdShape<128>::BM; }
+int fwd_block_m(int D, bool causal) {
+  if (D == 64) return causal ? FwdShape<64, 1>::BM : FwdShape<64, 2>::BM;
+  return FwdShape<128, 1>::BM;
+}
 
 hipError_t launch_fwd(int dtype, int D, const FwdParams& p, hipStream_t stream) {
-  if (dtype == 0) return D == 64 ? launch_typed<_Float16, 64>(p, stream) : launch_typed<_Float16, 128>(p, stream);
-  return D == 64 ? launch_typed<__bf16, 64>(p, stream) : launch_typed<__bf16, 128>(p, stream);
+  return dtype == 0 ? launch_dtype<_Float16>(D, p, stream) : launch_dtype<__bf16>(D, p, stream);
 }
 
 }  // namespace mea

@@ -42,7 +42,7 @@ struct DecParams {
 };
 
 // Query rows per forward work-group and the decode chunk length.
-int fwd_block_m(int D);
+int fwd_block_m(int D, bool causal);
 constexpr int kDecodeChunk = 512;
 
 hipError_t launch_fwd(int dtype, int D, const FwdParams& p, hipStream_t stream);

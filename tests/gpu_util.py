@@ -5,6 +5,10 @@ import numpy as np
 import torch
 
 TOL = {"fp16": 2e-3, "bf16": 1.6e-2}   # max-abs error against the fp64 oracle (fp32 accumulation)
+# Row log-sum-exp: the normaliser l sums P after P is rounded to the input type
+# (the weights P.V really uses), so |dl/l| <= 2^-9 (bf16) or 2^-11 (fp16) and
+# |d lse| <= that bound; the margin covers fp32 accumulation and the final log.
+LSE_TOL = {"fp16": 2.0 ** -11 * 1.25, "bf16": 2.0 ** -9 * 1.25}
 TORCH_DTYPE = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
