@@ -72,11 +72,17 @@ struct FwdShape {
   static constexpr int WPE = (D == 64 && QB == 1) ? 3 : 2;
 };
 
-template <typename T, int D, int QB_>
+// CS and AL select how the causal and ALiBi flags are known: 0 = off, 1 = on
+// (compile-time constants), 2 = read from p at run time. Causal launches
+// specialise both; the dense launch reads both at run time, which the
+// compiler schedules better than the fully specialised form.
+template <typename T, int D, int QB_, int CS, int AL>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE))) fwd_kernel(const FwdParams p) {
   using S = FwdShape<D, QB_>;
   using MF = Mfma<T>;
+  const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
+  const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
   typedef typename MF::v8 v8;
   constexpr int QB = S::QB, QW = S::QW, BM = S::BM, LDS = S::LDS, LDSK = S::LDSK, TILE = S::TILE;
   constexpr int CPR = S::CPR, NLD = S::NLD;
@@ -106,7 +112,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   if (!p.varlen) {
     M_s = p.M;
     N_s = p.N;
-    tile = p.causal ? (p.n_qtiles - 1 - t) : t;
+    tile = CAUSAL ? (p.n_qtiles - 1 - t) : t;
     qoff = (long long)b * p.q_bstride + (long long)h * D;
     koff = (long long)b * p.kv_bstride + (long long)g * D;
     lse_off = ((long long)b * p.Hq + h) * p.M;
@@ -123,7 +129,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
     }
     if (s >= p.B) return;
     const int in = t - acc;
-    tile = p.causal ? (ntile - 1 - in) : in;
+    tile = CAUSAL ? (ntile - 1 - in) : in;
     const int* sk = p.seqstart_k;
     const int k0 = min(max(sk[s], 0), p.N);
     const int k1 = min(max(sk[s + 1], k0), p.N);
@@ -137,17 +143,17 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   const int i0 = tile * BM;            // first query row of the work-group (segment-local)
   const int off = N_s - M_s;           // bottom-right causal alignment
   int kend = N_s;
-  if (p.causal) kend = min(N_s, i0 + BM + off);
+  if (CAUSAL) kend = min(N_s, i0 + BM + off);
   kend = max(kend, 0);
   const int ntiles = (kend + kBN - 1) / kBN;
 
   const int wq0 = i0 + wave * QW;      // first query row of this wave
   const int wlast = min(wq0 + QW, M_s) - 1;
   int wkend = 0;                       // keys this wave needs
-  if (wlast >= wq0) wkend = p.causal ? max(min(N_s, wlast + off + 1), 0) : N_s;
+  if (wlast >= wq0) wkend = CAUSAL ? max(min(N_s, wlast + off + 1), 0) : N_s;
 
   const float c = p.scale_log2;
-  const float slope = p.alibi ? p.slopes[h] * kLog2e : 0.f;
+  const float slope = ALIBI ? p.slopes[h] * kLog2e : 0.f;
 
   // ---- Q fragments (B operand: column = query, k = head dim) ---------------
   v8 qf[QB][DS];
@@ -210,12 +216,19 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   const int vrow = (g16 >> 1) * 4 + (ll >> 2);
   const int vcol = (g16 & 1) * 16 + 4 * (ll & 3);
 
-  if (ntiles > 0) gload(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  // Under ALiBi the bias grows towards the diagonal, so blocks are walked
+  // from the last one back to the first: the running maximum is then set by
+  // the first block and the lazy rescale almost never fires. Otherwise
+  // blocks go in order, so the work-groups of a head read the same K/V
+  // blocks at about the same time (L2 reuse).
+  const bool rev = CS == 1 && AL == 1;
+  if (ntiles > 0) gload(rev ? ntiles - 1 : 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt = rev ? ntiles - 1 - it : it;
+    const int buf = it & 1;
     lstore(buf);
     __syncthreads();
-    if (kt + 1 < ntiles) gload(kt + 1);
+    if (it + 1 < ntiles) gload(rev ? kt - 1 : kt + 1);
 
     const int key_base = kt * kBN;
     if (key_base >= wkend) continue;   // the whole block is masked for this wave
@@ -242,26 +255,35 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
     }
     __builtin_amdgcn_s_setprio(0);
 
-    const bool need_mask = (key_base + kBN > N_s) || (p.causal && key_base + kBN - 1 > wq0 + off);
+    const bool need_mask = (key_base + kBN > N_s) || (CAUSAL && key_base + kBN - 1 > wq0 + off);
     typename MF::v8 pf[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qi = wq0 + qb * 32 + l32;
       float cc = c;
-      if (p.alibi || need_mask) {
+      if (ALIBI || need_mask) {
         // Explicit scores in log2 units: scale, ALiBi from indices, mask.
         const int rel = key_base + hi * 4;           // key = rel + kr
         const int lim_n = N_s - rel;                 // kr <  lim_n : inside the segment
-        const int lim_c = p.causal ? (qi + off - rel) : 0x7fffffff;  // kr <= lim_c : causal
-        const float dist0 = (float)(qi + off - rel);
+        const int lim_c = CAUSAL ? (qi + off - rel) : 0x7fffffff;  // kr <= lim_c : causal
+        const float dist0 = (float)(qi + off - rel); // query position - key, at kr = 0
+        const float nb = -slope * dist0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
-            float x = s[qb][kb][r] * c;
-            if (p.alibi) x -= slope * fabsf(dist0 - (float)kr);
-            s[qb][kb][r] = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
+            float x;
+            if constexpr (CS == 1 && AL == 1) {
+              // Allowed keys have dist0 - kr >= 0, so |.| is not needed.
+              x = fmaf(s[qb][kb][r], c, fmaf(slope, (float)kr, nb));
+              if (need_mask) x = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
+            } else {
+              x = s[qb][kb][r] * c;
+              if (ALIBI) x -= slope * fabsf(dist0 - (float)kr);
+              x = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
+            }
+            s[qb][kb][r] = x;
           }
         cc = 1.f;
       }
@@ -350,17 +372,22 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   }
 }
 
-template <typename T, int D, int QB>
+template <typename T, int D, int QB, bool CAUSAL>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
   const int grid = p.wg_per_xcd * 8;
-  hipLaunchKernelGGL((fwd_kernel<T, D, QB>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  if (!CAUSAL)
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 2, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  else if (p.alibi)
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 1, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 1, 0>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
-  if (D == 64) return p.causal ? launch_typed<T, 64, 1>(p, stream) : launch_typed<T, 64, 2>(p, stream);
-  return launch_typed<T, 128, 1>(p, stream);
+  if (D == 64) return p.causal ? launch_typed<T, 64, 1, true>(p, stream) : launch_typed<T, 64, 2, false>(p, stream);
+  return p.causal ? launch_typed<T, 128, 1, true>(p, stream) : launch_typed<T, 128, 1, false>(p, stream);
 }
 
 }  // namespace
