@@ -44,6 +44,38 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per launch from profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE
+    and WRITE_SIZE, calibrated against a plain 1 GiB copy), or None for every
+    kernel once a kernel source differs from the one the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    csrc = os.path.join(ROOT, "memory_efficient_exact_tiled_amd", "csrc")
+    for name, sha in t["sources_sha256_16"].items():
+        cur = hashlib.sha256(open(os.path.join(csrc, name)).read().encode()).hexdigest()[:16]
+        if cur != sha:
+            return None
+    out = {}
+    for k, v in t["kernels"].items():
+        out[k] = v["fetch_bytes"] + v["write_bytes"]
+    return out
+
+
+def traffic_for(traffic, *needles):
+    if traffic is None:
+        return None
+    total = 0.0
+    for nd in needles:
+        hits = [v for k, v in traffic.items() if nd in k]
+        if len(hits) != 1:
+            return None
+        total += hits[0]
+    return round(total)
+
+
 def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -231,6 +263,7 @@ def main():
             per_item[n] = {"avg_launch_us": round(ms[n] * 1e3, 2), "gbs": round(dec_gbs, 1),
                            "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dec_bytes}
     head = tflops.get("fwd_noncausal")
+    traffic = measured_traffic()
 
     res = {
         "metric": "attn fwd TFLOP/s (bf16, M=4096, % MFMA peak); decode HBM GB/s",
@@ -254,13 +287,16 @@ def main():
         },
         "roofline": None if head is None else {
             "bound": "mfma", "achieved": round(head, 2), "peak": PEAK_MFMA_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(head / PEAK_MFMA_TFLOPS, 4), "traffic": None,
-            "kernel": "fwd_kernel<bf16,64>", "avg_launch_us": round(ms["fwd_noncausal"] * 1e3, 2),
+            "unit": "TFLOP/s", "frac": round(head / PEAK_MFMA_TFLOPS, 4),
+            "traffic": traffic_for(traffic, "fwd_kernelIDF16bLi64ELi2ELi2ELi2"),
+            "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+            "kernel": "fwd_kernel<bf16,64,QB=2>", "avg_launch_us": round(ms["fwd_noncausal"] * 1e3, 2),
             "algorithmic_flops": flops_all["fwd_noncausal"],
         },
         "roofline_decode": None if dec_gbs is None else {
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic_for(traffic, "decode_split_kernelIDF16bLi128", "decode_combine_kernelIDF16bLi128"),
             "kernel": "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
             "avg_launch_us": round(ms["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes,
         },
