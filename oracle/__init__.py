@@ -16,6 +16,8 @@ from .attention import (  # noqa: F401
     decode,
     decode_bits,
     fwd,
+    fwd_kvcache,
     fwd_rows,
+    kv_append,
     kv_head,
 )

@@ -180,3 +180,42 @@ def decode(q_bits, kcache_bits, vcache_bits, ctx_lens, dtype: str, scale: float,
         ob, _ = attend(qb, kb, vb, scale, causal=True, slopes=alibi_slopes)
         o[b] = ob[0]
     return o
+
+
+def fwd_kvcache(q_bits, kcache_bits, vcache_bits, ctx_lens, dtype: str, scale: float, causal: bool = True,
+                alibi_slopes=None, batches=None):
+    """The M newest queries of each sequence against its KV cache (chunked
+    prefill / multi-token decode).
+
+    q ``[B,M,Hq,D]`` holds the queries of positions ``ctx-M .. ctx-1`` of
+    sequence b, whose keys and values are already in the cache
+    ``[B,S_max,Hkv,D]``; they attend to cache rows ``0..ctx-1`` with the
+    bottom-right causal alignment of the briefia.fr KV-cache code (row i sees
+    keys j <= i + ctx - M). Returns ``(o [B,M,Hq,D], lse [B,Hq,M])``; rows of
+    batch entries not in ``batches`` are NaN.
+    """
+    B, M, Hq, D = q_bits.shape
+    o = np.full((B, M, Hq, D), np.nan)
+    lse = np.full((B, Hq, M), np.nan)
+    for b in (range(B) if batches is None else batches):
+        n = int(ctx_lens[b])
+        ob, lb = attend(decode_bits(q_bits[b], dtype), decode_bits(kcache_bits[b, :n], dtype),
+                        decode_bits(vcache_bits[b, :n], dtype), scale, causal, alibi_slopes)
+        o[b], lse[b] = ob, lb
+    return o, lse
+
+
+def kv_append(kcache_bits, vcache_bits, k_new_bits, v_new_bits, ctx_lens):
+    """Cache after appending T new rows per sequence at positions ctx..ctx+T-1
+    (rows that would fall past S_max are dropped). Bit patterns in, bit
+    patterns out: appending is a copy (briefia.fr page, section on the simple
+    KV cache: each decode step concatenates the new key and value)."""
+    kc, vc = np.array(kcache_bits, copy=True), np.array(vcache_bits, copy=True)
+    B, S_max = kc.shape[:2]
+    T = k_new_bits.shape[1]
+    for b in range(B):
+        c = int(ctx_lens[b])
+        n = max(0, min(T, S_max - c))
+        kc[b, c:c + n] = k_new_bits[b, :n]
+        vc[b, c:c + n] = v_new_bits[b, :n]
+    return kc, vc

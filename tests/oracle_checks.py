@@ -286,6 +286,43 @@ def check_fwd_rows_matches_fwd(orc):
     assert np.array_equal(orow, o[0, [6, 16]]), "fwd_rows segment"
 
 
+def check_kvcache_prefill(orc):
+    """Multi-token decode over a cache: with one query it is the decode step;
+    with M queries it is the last M rows of full causal attention over the
+    sequence (positions ctx-M..ctx-1), per batch row."""
+    B, S, Hq, Hkv, D, M = 3, 30, 4, 2, 8, 5
+    ctx = np.array([30, 12, 5], np.int32)
+    dec = inp.decode_case(23, ctx, S, Hq, Hkv, D, "bf16")
+    slopes = inp.alibi_slopes(Hq)
+    o1, _ = orc.fwd_kvcache(dec["q"][:, None], dec["kcache"], dec["vcache"], ctx, "bf16", 0.3, alibi_slopes=slopes)
+    od = orc.decode(dec["q"], dec["kcache"], dec["vcache"], ctx, "bf16", 0.3, alibi_slopes=slopes)
+    assert _maxerr(o1[:, 0], od) < TOL, "kvcache M=1 == decode"
+    for b in range(B):
+        n = int(ctx[b])
+        qfull = inp.normal_bits(31, (1, n, Hq, D), "bf16", b)
+        om, lm = orc.fwd_kvcache(qfull[:, n - M:], dec["kcache"][b:b + 1], dec["vcache"][b:b + 1], ctx[b:b + 1],
+                                 "bf16", 0.3, alibi_slopes=slopes)
+        of, lf = orc.fwd(qfull, dec["kcache"][b:b + 1, :n], dec["vcache"][b:b + 1, :n], "bf16", 0.3, causal=True,
+                         alibi_slopes=slopes)
+        assert _maxerr(om[0], of[0, n - M:]) < TOL, ("kvcache suffix rows", b)
+
+
+def check_kv_append(orc):
+    """Appending T rows then reading the first ctx+T rows == concatenation."""
+    B, S, Hkv, D, T = 3, 16, 2, 4, 5
+    ctx = np.array([0, 9, 14], np.int32)
+    kc = inp.normal_bits(40, (B, S, Hkv, D), "fp16", 0)
+    vc = inp.normal_bits(40, (B, S, Hkv, D), "fp16", 1)
+    kn = inp.normal_bits(41, (B, T, Hkv, D), "fp16", 0)
+    vn = inp.normal_bits(41, (B, T, Hkv, D), "fp16", 1)
+    k2, v2 = orc.kv_append(kc, vc, kn, vn, ctx)
+    for b in range(B):
+        c = int(ctx[b])
+        n = min(T, S - c)
+        assert np.array_equal(k2[b, :c + n], np.concatenate([kc[b, :c], kn[b, :n]])), "append k"
+        assert np.array_equal(v2[b, c + n:], vc[b, c + n:]), "append leaves the rest"
+
+
 ALL_CHECKS = [
     check_sdpa_nomask,
     check_sdpa_causal_square,
@@ -305,4 +342,6 @@ ALL_CHECKS = [
     check_chunked_prefill_is_suffix,
     check_lse_merge,
     check_fwd_rows_matches_fwd,
+    check_kvcache_prefill,
+    check_kv_append,
 ]

@@ -32,6 +32,9 @@ MUTANTS = {
     "bf16_decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "transposed_p": ("(e @ v[:, g, :]) / safe_l[:, None]",
                      "((e.T if e.shape[0] == e.shape[1] else e) @ v[:, g, :]) / safe_l[:, None]"),
+    "kvcache_drops_last_row": ("ob, lb = attend(decode_bits(q_bits[b], dtype), decode_bits(kcache_bits[b, :n], dtype),",
+                               "ob, lb = attend(decode_bits(q_bits[b], dtype), decode_bits(kcache_bits[b, :n - 1], dtype),"),
+    "kv_append_short": ("n = max(0, min(T, S_max - c))", "n = max(0, min(T, S_max - c - 1))"),
     "blockdiag_ignores_k_segments": ("return [(0, int(sq[s]), int(sq[s + 1]), int(sk[s]), int(sk[s + 1]))",
                                      "return [(0, int(sq[s]), int(sq[s + 1]), 0, int(sk[-1]))"),
 }
