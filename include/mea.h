@@ -89,6 +89,47 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out,
             const float* alibi_slopes, int dtype, float* lse, void* stream);
 
 /*
+ * mea_fwd_kvcache - chunked prefill / multi-token decode over a KV cache:
+ * the M newest queries of every sequence attend to that sequence's cached
+ * keys and values, whose rows for those M tokens are already appended. The
+ * causal mask is aligned bottom-right (query row i, at position
+ * ctx_lens[b]-M+i, sees cache rows j <= i + ctx_lens[b] - M), which is the
+ * mask the simple KV cache builds: a lower triangle shifted by the number of
+ * cached tokens ("Transformer : comprendre l'entrainement et l'inference",
+ * briefia.fr, section on the simple KV cache; the prefill vs decode section).
+ * Same kernels as mea_fwd, with each sequence's key count read from ctx_lens.
+ *
+ *   q, out   [B, M, Hq, D]
+ *   kcache   [B, S_max, Hkv, D]     vcache same
+ *   ctx_lens int32 device array [B], 0 <= ctx_lens[b] <= S_max; rows at or
+ *            past ctx_lens[b] are never read. If ctx_lens[b] < M under the
+ *            causal mask, the first M - ctx_lens[b] rows have no key: out 0.
+ * bias_kind  MEA_MASK_CAUSAL and/or MEA_BIAS_ALIBI (MEA_MASK_BLOCKDIAG is
+ *            MEA_EINVAL). lse, if given: [B, Hq, M].
+ * Other arguments and errors as mea_fwd. With M = 1 this is the decode step
+ * computed by the forward kernels (mea_decode is the faster path for it).
+ */
+int mea_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out,
+                    int B, int M, int Hq, int Hkv, int D, int S_max, float scale, unsigned bias_kind,
+                    const float* alibi_slopes, int dtype, float* lse, void* stream);
+
+/*
+ * mea_kv_append - appends T new key/value rows per sequence to a KV cache:
+ * rows k_new[b, t], v_new[b, t] go to cache row ctx_lens[b] + t, t < T
+ * (each decode step concatenates the newest key and value to the cache:
+ * briefia.fr page above, section on the simple KV cache). Rows that would
+ * land at or past S_max are dropped. ctx_lens is read, not updated: the
+ * caller adds T to its lengths.
+ *
+ *   kcache, vcache [B, S_max, Hkv, D] (written);  k_new, v_new [B, T, Hkv, D]
+ *   ctx_lens int32 device array [B], 0 <= ctx_lens[b] <= S_max.
+ *   T >= 0 (T = 0 is a no-op). dtype as mea_fwd; a bit-exact copy.
+ * Returns MEA_OK or an error status (nothing launched on error).
+ */
+int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new, const int32_t* ctx_lens, int B,
+                  int S_max, int Hkv, int D, int T, int dtype, void* stream);
+
+/*
  * mea_decode - one KV-cache decode step: each sequence's newest query
  * attends to all of its cached keys (its own key and value already
  * appended). Split-KV: the context is cut into fixed chunks, each chunk

@@ -5,10 +5,12 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 
 * :func:`fwd` - tiled exact attention forward (causal, packed block-diagonal,
   grouped-query, ALiBi);
-* :func:`decode` - one KV-cache decode step (split-KV partials + combine).
+* :func:`decode` - one KV-cache decode step (split-KV partials + combine);
+* :func:`fwd_kvcache` - chunked prefill / multi-token decode over a KV cache;
+* :func:`kv_append` - append new key/value rows to a KV cache.
 
 Import fails if the library has not been built
-(``python -m memory_efficient_exact_tiled_amd.build``).
+(``python memory_efficient_exact_tiled_amd/build.py``).
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
@@ -28,6 +30,8 @@ from ._binding import (  # noqa: F401
     decode_chunk,
     decode_workspace_bytes,
     fwd,
+    fwd_kvcache,
+    kv_append,
     lib,
     strerror,
     supported,

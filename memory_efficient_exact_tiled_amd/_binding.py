@@ -23,16 +23,20 @@ MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP = 0, 1, 2, 3, 4
 MEA_FP16, MEA_BF16 = 0, 1
 MEA_MASK_CAUSAL, MEA_MASK_BLOCKDIAG, MEA_BIAS_ALIBI = 1, 2, 4
 
-EXPORTS = ("mea_fwd", "mea_decode", "mea_decode_workspace_bytes", "mea_strerror",
-           "mea_supported", "mea_decode_chunk")
+EXPORTS = ("mea_fwd", "mea_fwd_kvcache", "mea_kv_append", "mea_decode", "mea_decode_workspace_bytes",
+           "mea_strerror", "mea_supported", "mea_decode_chunk")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m memory_efficient_exact_tiled_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python memory_efficient_exact_tiled_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i, _f, _u, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
 _lib.mea_fwd.restype = _i
 _lib.mea_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp, _i, _vp, _vp]
+_lib.mea_fwd_kvcache.restype = _i
+_lib.mea_fwd_kvcache.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _i, _vp, _vp]
+_lib.mea_kv_append.restype = _i
+_lib.mea_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
 _lib.mea_decode.restype = _i
 _lib.mea_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _vp]
 _lib.mea_decode_workspace_bytes.restype = _sz
@@ -175,3 +179,47 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, alibi_slo
                            float(scale), _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def fwd_kvcache(q, kcache, vcache, ctx_lens, *, causal: bool = True, alibi_slopes=None,
+                scale: float | None = None, out=None, lse=None, stream=None):
+    """Chunked prefill / multi-token decode (``mea_fwd_kvcache``): q ``[B,M,Hq,D]``
+    are the M newest tokens of each sequence, already appended to the caches
+    ``[B,S_max,Hkv,D]``; int32 ``ctx_lens`` ``[B]`` on the device."""
+    torch = _torch()
+    B, M, Hq, D = q.shape
+    Bc, S_max, Hkv, Dc = kcache.shape
+    if Bc != B or Dc != D or vcache.shape != kcache.shape:
+        raise ValueError("q and cache shapes disagree")
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise ValueError("q and caches must share a dtype")
+    if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
+        raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_cuda(q, kcache, vcache, ctx_lens, out, lse, alibi_slopes)
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kind = (MEA_MASK_CAUSAL if causal else 0) | (MEA_BIAS_ALIBI if alibi_slopes is not None else 0)
+    _check(_lib.mea_fwd_kvcache(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(ctx_lens), _ptr(out), B, M, Hq, Hkv, D,
+                                S_max, float(scale), kind, _ptr(alibi_slopes), _dtype_code(q), _ptr(lse),
+                                _stream(stream)))
+    return out
+
+
+def kv_append(kcache, vcache, k_new, v_new, ctx_lens, *, stream=None):
+    """Append ``k_new``/``v_new`` ``[B,T,Hkv,D]`` to the caches at rows
+    ``ctx_lens[b] ..`` (``mea_kv_append``). ``ctx_lens`` is not updated."""
+    torch = _torch()
+    B, S_max, Hkv, D = kcache.shape
+    Bn, T, Hn, Dn = k_new.shape
+    if (Bn, Hn, Dn) != (B, Hkv, D) or v_new.shape != k_new.shape or vcache.shape != kcache.shape:
+        raise ValueError("cache and new-row shapes disagree")
+    if len({kcache.dtype, vcache.dtype, k_new.dtype, v_new.dtype}) != 1:
+        raise ValueError("caches and new rows must share a dtype")
+    if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
+        raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_cuda(kcache, vcache, k_new, v_new, ctx_lens)
+    _check(_lib.mea_kv_append(_ptr(kcache), _ptr(vcache), _ptr(k_new), _ptr(v_new), _ptr(ctx_lens), B, S_max, Hkv,
+                              D, T, _dtype_code(kcache), _stream(stream)))
+    return kcache, vcache

@@ -1,7 +1,7 @@
 """Builds libmea.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Run ``python -m memory_efficient_exact_tiled_amd.build`` (or call
-:func:`build`). Objects go to ``_build/`` beside this file; the library is
+Run ``python memory_efficient_exact_tiled_amd/build.py`` (by path: importing
+the package would load the library being rebuilt), or call :func:`build`. Objects go to ``_build/`` beside this file; the library is
 written next to this file, where the binding loads it from.
 """
 from __future__ import annotations
@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmea.so")
-SOURCES = ["api.hip", "fwd.hip", "decode.hip"]
+SOURCES = ["api.hip", "fwd.hip", "decode.hip", "kvcache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -72,9 +72,14 @@ int mea_supported(int dtype, int D) { return (dtype_ok(dtype) && dim_ok(D)) ? 1 
 
 int mea_decode_chunk(void) { return mea::kDecodeChunk; }
 
-int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv, int D,
-            float scale, unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
-            const float* alibi_slopes, int dtype, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by mea_fwd and mea_fwd_kvcache: validates, fills FwdParams, launches.
+int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv, int D,
+             float scale, unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
+             const float* alibi_slopes, int dtype, float* lse, const int32_t* kv_lens, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return MEA_EINVAL;
   if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return MEA_EINVAL;
   if (Hq % Hkv != 0) return MEA_EINVAL;
@@ -104,6 +109,7 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M
   p.seqstart_q = seqstart_q;
   p.seqstart_k = seqstart_k != nullptr ? seqstart_k : seqstart_q;
   p.slopes = alibi_slopes;
+  p.kv_lens = kv_lens;
   p.B = B;
   p.M = M;
   p.N = N;
@@ -139,7 +145,57 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M
     if (rc == MEA_OK && seqstart_k != nullptr) rc = debug_check_seqstart(seqstart_k, B, N, st);
     if (rc != MEA_OK) return rc;
   }
+  if (mea_debug() && kv_lens != nullptr) {
+    const int rc = debug_check_ctx(kv_lens, B, N, st);
+    if (rc != MEA_OK) return rc;
+  }
   return mea::launch_fwd(dtype, D, p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv, int D,
+            float scale, unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
+            const float* alibi_slopes, int dtype, float* lse, void* stream) {
+  return fwd_impl(q, k, v, out, B, M, N, Hq, Hkv, D, scale, bias_kind, seqstart_q, seqstart_k, alibi_slopes, dtype,
+                  lse, nullptr, stream);
+}
+
+int mea_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out,
+                    int B, int M, int Hq, int Hkv, int D, int S_max, float scale, unsigned bias_kind,
+                    const float* alibi_slopes, int dtype, float* lse, void* stream) {
+  if (ctx_lens == nullptr) return MEA_EINVAL;
+  if ((bias_kind & MEA_MASK_BLOCKDIAG) != 0u) return MEA_EINVAL;
+  return fwd_impl(q, kcache, vcache, out, B, M, S_max, Hq, Hkv, D, scale, bias_kind, nullptr, nullptr, alibi_slopes,
+                  dtype, lse, ctx_lens, stream);
+}
+
+int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new, const int32_t* ctx_lens, int B,
+                  int S_max, int Hkv, int D, int T, int dtype, void* stream) {
+  if (kcache == nullptr || vcache == nullptr || k_new == nullptr || v_new == nullptr || ctx_lens == nullptr)
+    return MEA_EINVAL;
+  if (B <= 0 || S_max <= 0 || Hkv <= 0 || D <= 0 || T < 0) return MEA_EINVAL;
+  if (!mea_supported(dtype, D)) return MEA_EUNSUPPORTED;
+  if ((long long)Hkv * D > 0x7fffffffLL || B > 65535) return MEA_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mea_debug()) {
+    const int rc = debug_check_ctx(ctx_lens, B, S_max, st);
+    if (rc != MEA_OK) return rc;
+  }
+  if (T == 0) return MEA_OK;
+  mea::AppendParams p{};
+  p.kc = static_cast<uint16_t*>(kcache);
+  p.vc = static_cast<uint16_t*>(vcache);
+  p.kn = static_cast<const uint16_t*>(k_new);
+  p.vn = static_cast<const uint16_t*>(v_new);
+  p.ctx = ctx_lens;
+  p.B = B;
+  p.S_max = S_max;
+  p.T = T;
+  p.row_elems = Hkv * D;
+  return mea::launch_kv_append(p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
 }
 
 size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {

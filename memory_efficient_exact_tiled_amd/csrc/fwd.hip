@@ -111,7 +111,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   long long qoff, koff, lse_off;
   if (!p.varlen) {
     M_s = p.M;
-    N_s = p.N;
+    N_s = p.kv_lens != nullptr ? min(max(p.kv_lens[b], 0), p.N) : p.N;
     tile = CAUSAL ? (p.n_qtiles - 1 - t) : t;
     qoff = (long long)b * p.q_bstride + (long long)h * D;
     koff = (long long)b * p.kv_bstride + (long long)g * D;

@@ -15,6 +15,7 @@ struct FwdParams {
   const int32_t* seqstart_q;
   const int32_t* seqstart_k;
   const float* slopes;
+  const int32_t* kv_lens;  // dense mode only, nullable: per-batch key count (clamped to N)
   int B, M, N, Hq, Hkv, group;
   int causal, varlen, alibi;
   float scale_log2;      // scale * log2(e)
@@ -45,7 +46,17 @@ struct DecParams {
 int fwd_block_m(int D, bool causal);
 constexpr int kDecodeChunk = 512;
 
+struct AppendParams {
+  uint16_t* kc;
+  uint16_t* vc;
+  const uint16_t* kn;
+  const uint16_t* vn;
+  const int32_t* ctx;
+  int B, S_max, T, row_elems;  // row_elems = Hkv * D
+};
+
 hipError_t launch_fwd(int dtype, int D, const FwdParams& p, hipStream_t stream);
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(int dtype, int D, const DecParams& p, hipStream_t stream);
 
 }  // namespace mea

@@ -123,3 +123,25 @@ def test_single_hip_runtime_in_process():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_kvcache_entry_points_reject():
+    lib = mea.lib()
+    # mea_fwd_kvcache: missing ctx_lens, block-diagonal flag, bad D
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 1024, 0.1, 1, None, 1, None, None]
+    a = list(args); a[3] = None
+    assert lib.mea_fwd_kvcache(*a) == mea.MEA_EINVAL
+    a = list(args); a[12] = mea.MEA_MASK_BLOCKDIAG
+    assert lib.mea_fwd_kvcache(*a) == mea.MEA_EINVAL
+    a = list(args); a[3] = None; a[9] = 96
+    assert lib.mea_fwd_kvcache(*a) == mea.MEA_EINVAL
+    a = list(args); a[9] = 96
+    assert lib.mea_fwd_kvcache(*a) == mea.MEA_EUNSUPPORTED
+    # mea_kv_append: negative T, null cache, bad dtype
+    ap = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1024, 2, 128, 4, 1, None]
+    a = list(ap); a[9] = -1
+    assert lib.mea_kv_append(*a) == mea.MEA_EINVAL
+    a = list(ap); a[0] = None
+    assert lib.mea_kv_append(*a) == mea.MEA_EINVAL
+    a = list(ap); a[10] = 9
+    assert lib.mea_kv_append(*a) == mea.MEA_EUNSUPPORTED
