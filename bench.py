@@ -161,6 +161,67 @@ def cpu_baseline_decode(ctx, seconds):
                       f"{nbytes / 1e9:.3f} GB of K/V in {busy:.1f} s"}
 
 
+def naive_vs_mea_table(torch, inp, mea, B=4, H=16, D=64, seqlens=(512, 1024, 2048, 4096)):
+    """The xFormers tutorial's benchmark (chipsbuilder.com page, "Benchmark
+    Memoria e Velocita dell'Attenzione Classica"): time and peak memory of a
+    naive attention (the score matrix materialised: matmul, softmax, matmul in
+    torch) against the memory-efficient kernel, over sequence lengths. Timing
+    follows the page's method: 5 warmup calls, then the mean of 20 calls
+    between two events; peak memory is torch's max_memory_allocated after
+    resetting the peak. Shapes: B=4, H=16, D=64, bf16, no mask (the page does
+    not state its own)."""
+    def cuda_time(fn, iters=20, warmup=5):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / iters
+
+    def peak_mb(fn):
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() / 1e6
+
+    rows = []
+    for M in seqlens:
+        c = inp.dense_case(3, B, M, M, H, H, D, "bf16")
+        q, k, v = (to_dev(c[x], torch) for x in ("q", "k", "v"))
+        # [B,H,M,D] copies for the naive path; the key operand is transposed
+        # into a contiguous tensor before the batched product.
+        qh = q.permute(0, 2, 1, 3).contiguous()
+        kt = k.permute(0, 2, 3, 1).contiguous()
+        vh = v.permute(0, 2, 1, 3).contiguous()
+        scale = 1.0 / np.sqrt(D)
+
+        def naive():
+            sc = torch.matmul(qh, kt) * scale
+            p = torch.softmax(sc.float(), dim=-1).to(torch.bfloat16)
+            return torch.matmul(p, vh)
+
+        def memeff():
+            return mea.fwd(q, k, v, scale=scale)
+
+        o_n = naive().permute(0, 2, 1, 3).float()
+        o_m = memeff().float()
+        diff = float((o_n - o_m).abs().max())
+        row = {"seqlen": M, "naive_mb": round(peak_mb(naive), 1), "mea_mb": round(peak_mb(memeff), 1),
+               "naive_ms": round(cuda_time(naive), 3), "mea_ms": round(cuda_time(memeff), 3),
+               "max_abs_diff": diff}
+        row["speedup"] = round(row["naive_ms"] / row["mea_ms"], 2)
+        rows.append(row)
+        log(f"[table] {row}")
+        del q, k, v, qh, kt, vh
+    print(json.dumps({"table": "naive vs memory-efficient attention forward", "shape": {"B": B, "H": H, "D": D},
+                      "dtype": "bf16", "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +231,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode",
                     help="comma-separated subset of the step to run (for profiling one kernel)")
+    ap.add_argument("--table", action="store_true",
+                    help="reproduce the tutorial's naive-vs-memory-efficient table (ms, peak MB) for seqlen 512..4096")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -185,6 +248,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.table:
+        naive_vs_mea_table(torch, inp, mea)
+        return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
