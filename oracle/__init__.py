@@ -13,6 +13,8 @@ only).
 """
 from .attention import (  # noqa: F401
     attend,
+    attend_grad,
+    bwd,
     decode,
     decode_bits,
     fwd,

@@ -43,7 +43,16 @@ Readings taken where the pages are silent (each also listed in the design doc):
 * a query row with no allowed key returns o = 0 and lse = -inf;
 * decode: the newest token's k/v is already in the cache (briefia.fr page,
   section "Pre-remplissage et decodage"); its query, at position ctx-1,
-  attends to cache rows 0..ctx-1.
+  attends to cache rows 0..ctx-1;
+* backward: the gradients of the loss sum(dO * o) with respect to q, k and v
+  (not the slopes, not the scale), for an upstream gradient dO. The
+  FlashAttention page (section on the softmax that needs not see the whole
+  row) says only that the backward recomputes the scores instead of storing
+  them; the gradient itself is the derivative of the definition above, written
+  out with the softmax Jacobian: dP = dO v^T, dS = P * (dP - rowsum(P * dP)),
+  dq = scale dS k, dk = scale dS^T q, dv = P^T dO. A KV head shared by several
+  query heads (GQA) receives the sum over them; rows with no allowed key
+  contribute nothing.
 """
 from __future__ import annotations
 
@@ -219,3 +228,73 @@ def kv_append(kcache_bits, vcache_bits, k_new_bits, v_new_bits, ctx_lens):
         kc[b, c:c + n] = k_new_bits[b, :n]
         vc[b, c:c + n] = v_new_bits[b, :n]
     return kc, vc
+
+
+def attend_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                causal: bool = False, slopes=None):
+    """Gradients of sum(do * attend(q, k, v)[0]) for one segment, float64.
+
+    q, do ``[M, Hq, D]``; k, v ``[N, Hkv, D]``. The attention weights are
+    recomputed from q and k (nothing from the forward is reused). Returns
+    ``(dq [M,Hq,D], dk [N,Hkv,D], dv [N,Hkv,D])``.
+    """
+    M, Hq, D = q.shape
+    N, Hkv, _ = k.shape
+    if do.shape != q.shape or v.shape != k.shape or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    sc = float(np.float32(scale))
+    dq = np.zeros((M, Hq, D))
+    dk = np.zeros((N, Hkv, D))
+    dv = np.zeros((N, Hkv, D))
+    if M == 0 or N == 0:
+        return dq, dk, dv
+    i = np.arange(M)
+    j = np.arange(N)
+    pos = i + (N - M)
+    allowed = (j[None, :] <= pos[:, None]) if causal else np.ones((M, N), dtype=bool)
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        s = sc * (q[:, h, :] @ k[:, g, :].T)
+        if slopes is not None:
+            s = s - float(np.float32(slopes[h])) * np.abs(pos[:, None] - j[None, :]).astype(np.float64)
+        s = np.where(allowed, s, -np.inf)
+        m = s.max(axis=1, initial=-np.inf)
+        m = np.where(np.isfinite(m), m, 0.0)
+        e = np.where(allowed, np.exp(s - m[:, None]), 0.0)
+        tot = e.sum(axis=1, keepdims=True)
+        p = e / np.where(tot > 0, tot, 1.0)             # rows with no key: p = 0
+        dp = do[:, h, :] @ v[:, g, :].T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq[:, h, :] = sc * (ds @ k[:, g, :])
+        dk[:, g, :] += sc * (ds.T @ q[:, h, :])
+        dv[:, g, :] += p.T @ do[:, h, :]
+    return dq, dk, dv
+
+
+def bwd(q_bits, k_bits, v_bits, do_bits, dtype: str, scale: float, causal: bool = False,
+        seqstart_q=None, seqstart_k=None, alibi_slopes=None, batches=None):
+    """Backward of :func:`fwd` over bit-pattern inputs (same layouts; ``do``
+    shaped like q). Returns float64 ``(dq, dk, dv)`` shaped like q, k, v.
+    Dense batch rows not in ``batches`` are left NaN (packed inputs are one row)."""
+    q = decode_bits(q_bits, dtype)
+    k = decode_bits(k_bits, dtype)
+    v = decode_bits(v_bits, dtype)
+    do = decode_bits(do_bits, dtype)
+    B, M = q.shape[:2]
+    N = k.shape[1]
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    keep = set(range(B) if batches is None else batches)
+    for b in keep:
+        dk[b] = 0.0
+        dv[b] = 0.0
+        dq[b] = 0.0
+    for b, q0, q1, k0, k1 in _segments(B, M, N, seqstart_q, seqstart_k):
+        if b not in keep:
+            continue
+        g = attend_grad(q[b, q0:q1], k[b, k0:k1], v[b, k0:k1], do[b, q0:q1], scale, causal, alibi_slopes)
+        dq[b, q0:q1] = g[0]
+        dk[b, k0:k1] = g[1]
+        dv[b, k0:k1] = g[2]
+    return dq, dk, dv

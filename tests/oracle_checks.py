@@ -323,6 +323,148 @@ def check_kv_append(orc):
         assert np.array_equal(v2[b, c + n:], vc[b, c + n:]), "append leaves the rest"
 
 
+
+# --- backward ----------------------------------------------------------------
+
+def _autograd_sdpa(q, k, v, do, scale, causal=False, mask=None, gqa=False):
+    """torch float64 autograd through SDPA on the CPU; tensors [B,M,H,D]."""
+    qt, kt, vt = (x.permute(0, 2, 1, 3).clone().requires_grad_(True) for x in (q, k, v))
+    out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, is_causal=causal, scale=scale, enable_gqa=gqa)
+    out.backward(do.permute(0, 2, 1, 3))
+    return [x.grad.permute(0, 2, 1, 3).numpy() for x in (qt, kt, vt)]
+
+
+def check_bwd_autograd_sdpa(orc):
+    """Gradients against torch's own autograd of SDPA in float64 (no mask,
+    causal, GQA with the KV gradient summed over each group)."""
+    cases = [(31, (2, 9, 13, 3, 3, 8), "fp16", False), (32, (1, 17, 17, 2, 2, 16), "bf16", True),
+             (33, (2, 12, 12, 6, 2, 8), "bf16", True), (34, (1, 7, 15, 4, 1, 8), "fp16", False)]
+    for seed, (B, M, N, Hq, Hkv, D), dt, causal in cases:
+        c = inp.dense_case(seed, B, M, N, Hq, Hkv, D, dt)
+        do = inp.normal_bits(seed + 100, (B, M, Hq, D), dt, 0)
+        scale = 0.37
+        g = orc.bwd(c["q"], c["k"], c["v"], do, dt, scale, causal=causal)
+        ref = _autograd_sdpa(*(_torch_decode(x, dt) for x in (c["q"], c["k"], c["v"], do)),
+                             float(np.float32(scale)), causal=causal, gqa=Hq != Hkv)
+        for name, a, r in zip("qkv", g, ref):
+            assert _maxerr(a, r) < TOL, ("bwd autograd", seed, name, _maxerr(a, r))
+
+
+def check_bwd_autograd_alibi_causal(orc):
+    """ALiBi under the causal mask: autograd of SDPA with the key-only float
+    bias slope*j (a different but softmax-equivalent bias) gives the same
+    gradients; the bias depends on no input, so it only enters through P."""
+    B, M, H, D = 1, 14, 3, 8
+    c = inp.dense_case(35, B, M, M, H, H, D, "bf16")
+    do = inp.normal_bits(135, (B, M, H, D), "bf16", 0)
+    slopes = inp.alibi_slopes(H)
+    g = orc.bwd(c["q"], c["k"], c["v"], do, "bf16", 0.3, causal=True, alibi_slopes=slopes)
+    j = torch.arange(M, dtype=torch.float64)
+    causal = torch.ones(M, M, dtype=torch.bool).tril()
+    mask = torch.where(causal[None], torch.from_numpy(slopes.astype(np.float64))[:, None, None] * j[None, None, :],
+                       torch.tensor(-float("inf"), dtype=torch.float64))
+    ref = _autograd_sdpa(*(_torch_decode(x, "bf16") for x in (c["q"], c["k"], c["v"], do)),
+                         float(np.float32(0.3)), mask=mask[None])
+    for name, a, r in zip("qkv", g, ref):
+        assert _maxerr(a, r) < TOL, ("bwd alibi", name, _maxerr(a, r))
+
+
+def check_bwd_finite_difference(orc):
+    """Directional derivatives of the forward (central differences of
+    ``attend``) against <grad, direction>, in the cases no library covers:
+    ALiBi without a mask, bottom-right causal with M > N (rows with no key)
+    and M < N, GQA."""
+    rng = np.random.default_rng(36)
+    for M, N, Hq, Hkv, causal, slopes in [(5, 8, 4, 2, False, np.float32([0.5, 0.25, 0.125, 0.0625])),
+                                          (7, 4, 2, 1, True, np.float32([0.3, 0.7])),
+                                          (3, 9, 2, 2, True, None)]:
+        D = 4
+        q, do = rng.standard_normal((2, M, Hq, D))
+        k, v = rng.standard_normal((2, N, Hkv, D))
+        scale = 0.6
+        grads = orc.attend_grad(q, k, v, do, scale, causal, slopes)
+        eps = 1e-5
+        for idx, x in enumerate((q, k, v)):
+            d = rng.standard_normal(x.shape)
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[idx] = x + eps * d
+            args_m[idx] = x - eps * d
+            fp = np.sum(do * orc.attend(*args_p, scale, causal, slopes)[0])
+            fm = np.sum(do * orc.attend(*args_m, scale, causal, slopes)[0])
+            fd = (fp - fm) / (2 * eps)
+            an = float(np.sum(grads[idx] * d))
+            assert abs(fd - an) < 1e-7 * max(1.0, abs(an)), ("finite difference", "qkv"[idx], M, N, fd, an)
+
+
+def check_bwd_zero_query_closed_form(orc):
+    """q = 0, causal, dO = 1: P is uniform over keys 0..i, so
+    dv_j = sum_{i >= j} 1/(i+1) = H_M - H_j (harmonic numbers), dk = 0 (every
+    term carries q), and dq_i = scale * sum_{j<=i} (w_j - mean w) k_j / (i+1)
+    with w_j = sum_d v_j (the covariance of w and k over the allowed keys)."""
+    M, D = 8, 4
+    q = np.zeros((1, M, 1, D), np.uint16)
+    c = inp.dense_case(37, 1, M, M, 1, 1, D, "fp16")
+    do = _ones_bits((1, M, 1, D), "fp16")
+    dq, dk, dv = orc.bwd(q, c["k"], c["v"], do, "fp16", 0.5, causal=True)
+    harmonic = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, M + 1))])
+    for jj in range(M):
+        assert abs(dv[0, jj, 0, 0] - (harmonic[M] - harmonic[jj])) < TOL, ("dv harmonic", jj)
+    assert np.all(dk == 0), "dk with q = 0"
+    k = orc.decode_bits(c["k"], "fp16")[0, :, 0]
+    w = orc.decode_bits(c["v"], "fp16")[0, :, 0].sum(axis=1)
+    for i in range(M):
+        cov = ((w[:i + 1] - w[:i + 1].mean())[:, None] * k[:i + 1]).sum(axis=0) / (i + 1)
+        assert _maxerr(dq[0, i, 0], 0.5 * cov) < TOL, ("dq covariance", i)
+
+
+def check_bwd_constant_v(orc):
+    """v constant across keys: the output no longer depends on q or k, so
+    dq = dk = 0; and every row's weights sum to one, so the dv rows add up
+    to the sum of dO over the rows that see any key."""
+    B, M, N, Hq, Hkv, D = 1, 6, 9, 4, 2, 8
+    c = inp.dense_case(38, B, M, N, Hq, Hkv, D, "bf16")
+    row = c["v"][:, :1]
+    vconst = np.repeat(row, N, axis=1)
+    do = inp.normal_bits(138, (B, M, Hq, D), "bf16", 0)
+    for causal, slopes in [(False, None), (True, inp.alibi_slopes(Hq))]:
+        dq, dk, dv = orc.bwd(c["q"], c["k"], vconst, do, "bf16", 0.4, causal=causal, alibi_slopes=slopes)
+        assert _maxerr(dq, 0.0) < TOL and _maxerr(dk, 0.0) < TOL, ("constant v", causal)
+    dof = orc.decode_bits(do, "bf16")
+    dq, dk, dv = orc.bwd(c["q"], c["k"], c["v"], do, "bf16", 0.4, causal=True)
+    for g in range(Hkv):
+        want = dof[0, :, g * 2:(g + 1) * 2].sum(axis=(0, 1))
+        assert _maxerr(dv[0, :, g].sum(axis=0), want) < 1e-10, ("dv column sums", g)
+        assert _maxerr(dk[0, :, g].sum(axis=0), 0.0) < 1e-10, ("dk sums to zero", g)
+
+
+def check_bwd_blockdiag_and_gqa(orc):
+    """Packed backward == each segment's own backward; GQA backward == K/V
+    repeated per query head with the repeats' gradients summed."""
+    lengths = [4, 0, 7, 2]
+    vc = inp.varlen_case(39, lengths, 4, 2, 8, "fp16")
+    do = inp.normal_bits(139, vc["q"].shape, "fp16", 0)
+    st = vc["seqstart"]
+    for causal, slopes in [(False, None), (True, inp.alibi_slopes(4))]:
+        dq, dk, dv = orc.bwd(vc["q"], vc["k"], vc["v"], do, "fp16", 0.3, causal=causal,
+                             seqstart_q=st, alibi_slopes=slopes)
+        for s_ in range(len(lengths)):
+            a, b = st[s_], st[s_ + 1]
+            g = orc.bwd(vc["q"][:, a:b], vc["k"][:, a:b], vc["v"][:, a:b], do[:, a:b], "fp16", 0.3,
+                        causal=causal, alibi_slopes=slopes)
+            assert np.array_equal(dq[:, a:b], g[0]) and np.array_equal(dk[:, a:b], g[1]) \
+                and np.array_equal(dv[:, a:b], g[2]), ("bwd blockdiag", causal, s_)
+    c = inp.dense_case(40, 2, 9, 9, 6, 2, 8, "bf16")
+    do = inp.normal_bits(140, (2, 9, 6, 8), "bf16", 0)
+    for causal in (False, True):
+        g = orc.bwd(c["q"], c["k"], c["v"], do, "bf16", 0.3, causal=causal)
+        r = orc.bwd(c["q"], np.repeat(c["k"], 3, axis=2), np.repeat(c["v"], 3, axis=2), do, "bf16", 0.3,
+                    causal=causal)
+        assert np.array_equal(g[0], r[0]), ("bwd gqa dq", causal)
+        for a, rr in zip(g[1:], r[1:]):
+            summed = rr.reshape(2, 9, 2, 3, 8).sum(axis=3)
+            assert _maxerr(a, summed) < TOL, ("bwd gqa dk/dv", causal)
+
 ALL_CHECKS = [
     check_sdpa_nomask,
     check_sdpa_causal_square,
@@ -344,4 +486,10 @@ ALL_CHECKS = [
     check_fwd_rows_matches_fwd,
     check_kvcache_prefill,
     check_kv_append,
+    check_bwd_autograd_sdpa,
+    check_bwd_autograd_alibi_causal,
+    check_bwd_finite_difference,
+    check_bwd_zero_query_closed_form,
+    check_bwd_constant_v,
+    check_bwd_blockdiag_and_gqa,
 ]

@@ -37,6 +37,21 @@ MUTANTS = {
     "kv_append_short": ("n = max(0, min(T, S_max - c))", "n = max(0, min(T, S_max - c - 1))"),
     "blockdiag_ignores_k_segments": ("return [(0, int(sq[s]), int(sq[s + 1]), int(sk[s]), int(sk[s + 1]))",
                                      "return [(0, int(sq[s]), int(sq[s + 1]), 0, int(sk[-1]))"),
+    "bwd_drops_delta": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "bwd_delta_wrong_axis": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))",
+                             "ds = p * (dp - (p * dp).sum(axis=0, keepdims=True))"),
+    "bwd_dq_no_scale": ("dq[:, h, :] = sc * (ds @ k[:, g, :])", "dq[:, h, :] = (ds @ k[:, g, :])"),
+    "bwd_dk_ds_untransposed": ("dk[:, g, :] += sc * (ds.T @ q[:, h, :])",
+                               "dk[:, g, :] += sc * ((ds if M == N else ds.T) @ q[:, h, :])"),
+    "bwd_dv_p_untransposed": ("dv[:, g, :] += p.T @ do[:, h, :]", "dv[:, g, :] += (p if M == N else p.T) @ do[:, h, :]"),
+    "bwd_gqa_overwrites": ("dv[:, g, :] += p.T @ do[:, h, :]", "dv[:, g, :] = p.T @ do[:, h, :]"),
+    "bwd_dp_uses_k": ("dp = do[:, h, :] @ v[:, g, :].T", "dp = do[:, h, :] @ k[:, g, :].T"),
+    "bwd_dk_uses_k": ("dk[:, g, :] += sc * (ds.T @ q[:, h, :])", "dk[:, g, :] += sc * (ds.T @ k[:, g, :][:M] if M <= N else ds.T @ q[:, h, :])"),
+    "bwd_unmasked": ("allowed = (j[None, :] <= pos[:, None]) if causal else np.ones((M, N), dtype=bool)",
+                     "allowed = np.ones((M, N), dtype=bool)"),
+    "bwd_top_left": ("pos = i + (N - M)", "pos = i"),
+    "bwd_alibi_sign": ("s = s - float(np.float32(slopes[h])) * np.abs", "s = s + float(np.float32(slopes[h])) * np.abs"),
+    "bwd_unnormalised_p": ("p = e / np.where(tot > 0, tot, 1.0)", "p = e"),
 }
 
 
