@@ -35,7 +35,7 @@ extern "C" {
 #define MEA_OK 0
 #define MEA_EINVAL 1       /* null pointer, non-positive size, inconsistent heads, bad scale */
 #define MEA_EUNSUPPORTED 2 /* (dtype, head dim) combination without a kernel */
-#define MEA_EWORKSPACE 3   /* decode workspace missing or too small */
+#define MEA_EWORKSPACE 3   /* workspace missing, too small or not 256-byte aligned */
 #define MEA_EHIP 4         /* the HIP runtime rejected a launch */
 
 /* Element types of q, k, v, caches and outputs. */
@@ -87,6 +87,43 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out,
             int B, int M, int N, int Hq, int Hkv, int D, float scale,
             unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
             const float* alibi_slopes, int dtype, float* lse, void* stream);
+
+/*
+ * mea_bwd - backward pass of mea_fwd: the gradients dq, dk, dv of the loss
+ * sum(dout * out) for the same (q, k, v, masks, bias). The scores are
+ * recomputed block by block from q, k and the forward's lse, never stored
+ * ("FlashAttention (2022): l'attenzione che non satura la memoria",
+ * paithon.it, section on the softmax that needs not see the whole row: the
+ * backward recomputes the score matrix on the fly). With P = exp(s - lse):
+ *
+ *   dP = dout v^T,  dS = P * (dP - rowsum(dout * out)),
+ *   dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout
+ *
+ * (the derivative of mea_fwd's definition through the softmax). Under
+ * grouped-query attention dk, dv of a KV head sum over its query heads.
+ * Training context: the xFormers tutorial's mixed-precision training section
+ * (chipsbuilder.com page above).
+ *
+ *   q, out, dout, dq   layout of mea_fwd's q      k, v, dk, dv  layout of k
+ *   lse     the fp32 log-sum-exp mea_fwd wrote for this (q, k, v) (required)
+ *   out     mea_fwd's output for the same inputs
+ * B, M, N, Hq, Hkv, D, scale, bias_kind, seqstart_q, seqstart_k,
+ * alibi_slopes, dtype: exactly as in the mea_fwd call.
+ * dq, dk, dv are fully overwritten (keys no query sees get 0); they must not
+ * alias any input.
+ * workspace  device buffer of at least mea_bwd_workspace_bytes(B, M, Hq,
+ *            bias_kind) bytes, 256-byte aligned, owned by the caller;
+ *            contents on entry ignored. Concurrent calls must not share it.
+ * Accumulation is fp32; P and dS are rounded to the input type before their
+ * products (as P in the forward); every gradient element has one writer, so
+ * results are deterministic run to run.
+ * Returns MEA_OK or an error status (nothing launched on error).
+ */
+size_t mea_bwd_workspace_bytes(int B, int M, int Hq, unsigned bias_kind);
+int mea_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D, float scale,
+            unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k, const float* alibi_slopes,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mea_fwd_kvcache - chunked prefill / multi-token decode over a KV cache:

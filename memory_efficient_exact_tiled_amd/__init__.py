@@ -5,6 +5,7 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 
 * :func:`fwd` - tiled exact attention forward (causal, packed block-diagonal,
   grouped-query, ALiBi);
+* :func:`bwd` - its backward (dq, dk, dv with the scores recomputed);
 * :func:`decode` - one KV-cache decode step (split-KV partials + combine);
 * :func:`fwd_kvcache` - chunked prefill / multi-token decode over a KV cache;
 * :func:`kv_append` - append new key/value rows to a KV cache.
@@ -26,6 +27,8 @@ from ._binding import (  # noqa: F401
     MEA_MASK_CAUSAL,
     MEA_OK,
     MeaError,
+    bwd,
+    bwd_workspace_bytes,
     decode,
     decode_chunk,
     decode_workspace_bytes,

@@ -23,8 +23,8 @@ MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP = 0, 1, 2, 3, 4
 MEA_FP16, MEA_BF16 = 0, 1
 MEA_MASK_CAUSAL, MEA_MASK_BLOCKDIAG, MEA_BIAS_ALIBI = 1, 2, 4
 
-EXPORTS = ("mea_fwd", "mea_fwd_kvcache", "mea_kv_append", "mea_decode", "mea_decode_workspace_bytes",
-           "mea_strerror", "mea_supported", "mea_decode_chunk")
+EXPORTS = ("mea_fwd", "mea_bwd", "mea_bwd_workspace_bytes", "mea_fwd_kvcache", "mea_kv_append", "mea_decode",
+           "mea_decode_workspace_bytes", "mea_strerror", "mea_supported", "mea_decode_chunk")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python memory_efficient_exact_tiled_amd/build.py`")
@@ -33,6 +33,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i, _f, _u, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
 _lib.mea_fwd.restype = _i
 _lib.mea_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp, _i, _vp, _vp]
+_lib.mea_bwd.restype = _i
+_lib.mea_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp,
+                         _i, _vp, _sz, _vp]
+_lib.mea_bwd_workspace_bytes.restype = _sz
+_lib.mea_bwd_workspace_bytes.argtypes = [_i, _i, _i, _u]
 _lib.mea_fwd_kvcache.restype = _i
 _lib.mea_fwd_kvcache.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _i, _vp, _vp]
 _lib.mea_kv_append.restype = _i
@@ -74,6 +79,10 @@ def decode_chunk() -> int:
 
 def decode_workspace_bytes(B: int, Hq: int, D: int, S_max: int) -> int:
     return int(_lib.mea_decode_workspace_bytes(B, Hq, D, S_max))
+
+
+def bwd_workspace_bytes(B: int, M: int, Hq: int, bias_kind: int) -> int:
+    return int(_lib.mea_bwd_workspace_bytes(B, M, Hq, bias_kind))
 
 
 def _check(status: int) -> None:
@@ -151,6 +160,59 @@ def fwd(q, k, v, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alib
                         _ptr(seqstart_q), _ptr(seqstart_k), _ptr(alibi_slopes), _dtype_code(q), _ptr(lse),
                         _stream(stream)))
     return out
+
+
+def _shapes(q, k, seqstart_q, seqstart_k):
+    torch = _torch()
+    if seqstart_q is not None:
+        M, Hq, D = q.shape[-3:]
+        N, Hkv, _ = k.shape[-3:]
+        if q.numel() != M * Hq * D or k.numel() != N * Hkv * D:
+            raise ValueError("packed q/k must be [1,T,H,D] or [T,H,D]")
+        for s in (seqstart_q, seqstart_k):
+            if s is not None and (s.dtype != torch.int32 or not s.is_cuda):
+                raise TypeError("seqstart arrays must be int32 device tensors")
+        return seqstart_q.numel() - 1, M, N, Hq, Hkv, D
+    B, M, Hq, D = q.shape
+    Bk, N, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("q and k shapes disagree")
+    return B, M, N, Hq, Hkv, D
+
+
+def bwd(q, k, v, out, dout, lse, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alibi_slopes=None,
+        scale: float | None = None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of :func:`fwd` (``mea_bwd``): gradients of ``sum(dout * out)``.
+
+    ``out`` and ``lse`` are what :func:`fwd` returned/filled for the same
+    arguments; ``dout`` is shaped like q. The workspace is allocated with torch
+    when not given. Returns ``(dq, dk, dv)``.
+    """
+    torch = _torch()
+    B, M, N, Hq, Hkv, D = _shapes(q, k, seqstart_q, seqstart_k)
+    if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("v must match k, out and dout must match q")
+    if len({q.dtype, k.dtype, v.dtype, out.dtype, dout.dtype}) != 1:
+        raise ValueError("q, k, v, out, dout must share a dtype")
+    if lse.dtype != torch.float32 or lse.numel() != (1 if seqstart_q is not None else B) * Hq * M:
+        raise ValueError("lse must be the float32 [B,Hq,M] (packed [Hq,M]) array the forward filled")
+    if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
+        raise TypeError("alibi_slopes must be float32")
+    _need_cuda(q, k, v, out, dout, lse, dq, dk, dv, alibi_slopes, workspace)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    kind = ((MEA_MASK_CAUSAL if causal else 0) | (MEA_MASK_BLOCKDIAG if seqstart_q is not None else 0)
+            | (MEA_BIAS_ALIBI if alibi_slopes is not None else 0))
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(B, M, Hq, kind), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(_lib.mea_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, M, N, Hq, Hkv, D, float(scale), kind, _ptr(seqstart_q), _ptr(seqstart_k),
+                        _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, alibi_slopes=None, out=None,

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmea.so")
-SOURCES = ["api.hip", "fwd.hip", "decode.hip", "kvcache.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "decode.hip", "kvcache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -62,7 +62,7 @@ const char* mea_strerror(int status) {
     case MEA_OK: return "success";
     case MEA_EINVAL: return "invalid argument";
     case MEA_EUNSUPPORTED: return "unsupported dtype or head dimension";
-    case MEA_EWORKSPACE: return "decode workspace missing or too small";
+    case MEA_EWORKSPACE: return "workspace missing, too small or misaligned";
     case MEA_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -196,6 +196,103 @@ int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_n
   p.T = T;
   p.row_elems = Hkv * D;
   return mea::launch_kv_append(p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
+}
+
+size_t mea_bwd_workspace_bytes(int B, int M, int Hq, unsigned bias_kind) {
+  if (B <= 0 || M <= 0 || Hq <= 0) return 0;
+  const size_t rows = ((bias_kind & MEA_MASK_BLOCKDIAG) != 0u ? 1u : (size_t)B) * (size_t)M;
+  const size_t one = ((rows * (size_t)Hq * sizeof(float)) + 255) & ~(size_t)255;
+  return 2 * one;
+}
+
+int mea_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D, float scale,
+            unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k, const float* alibi_slopes,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return MEA_EINVAL;
+  if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return MEA_EINVAL;
+  if (Hq % Hkv != 0) return MEA_EINVAL;
+  if ((bias_kind & ~(MEA_MASK_CAUSAL | MEA_MASK_BLOCKDIAG | MEA_BIAS_ALIBI)) != 0u) return MEA_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return MEA_EINVAL;
+  const bool varlen = (bias_kind & MEA_MASK_BLOCKDIAG) != 0u;
+  const bool causal = (bias_kind & MEA_MASK_CAUSAL) != 0u;
+  const bool alibi = (bias_kind & MEA_BIAS_ALIBI) != 0u;
+  if (alibi && alibi_slopes == nullptr) return MEA_EINVAL;
+  if (varlen) {
+    if (seqstart_q == nullptr) return MEA_EINVAL;
+    if (seqstart_k == nullptr && M != N) return MEA_EINVAL;
+  }
+  if (!mea_supported(dtype, D)) return MEA_EUNSUPPORTED;
+  const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
+  if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
+  const size_t need = mea_bwd_workspace_bytes(B, M, Hq, bias_kind);
+  if (workspace == nullptr || workspace_bytes < need) return MEA_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return MEA_EWORKSPACE;
+
+  mea::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.lse2 = static_cast<float*>(workspace);
+  p.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  p.seqstart_q = seqstart_q;
+  p.seqstart_k = seqstart_k != nullptr ? seqstart_k : seqstart_q;
+  p.slopes = alibi_slopes;
+  p.B = B;
+  p.M = M;
+  p.N = N;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.varlen = varlen;
+  p.alibi = alibi;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q_rstride = (int)q_rstride;
+  p.kv_rstride = (int)kv_rstride;
+  const long long TQ = mea::kBwdTileQ, TK = mea::kBwdTileK;
+  long long qt, kt, tq, tk;
+  if (varlen) {
+    p.rows = M;
+    qt = ((long long)M + TQ - 1) / TQ + B;   // each segment wastes at most one partial tile
+    kt = ((long long)N + TK - 1) / TK + B;
+    tq = qt * Hq;
+    tk = kt * Hkv;
+    p.q_bstride = 0;
+    p.kv_bstride = 0;
+  } else {
+    p.rows = (long long)B * M;
+    qt = ((long long)M + TQ - 1) / TQ;
+    kt = ((long long)N + TK - 1) / TK;
+    tq = qt * Hq * (long long)B;
+    tk = kt * Hkv * (long long)B;
+    p.q_bstride = (long long)M * q_rstride;
+    p.kv_bstride = (long long)N * kv_rstride;
+  }
+  if (tq > 0x7fffffffLL - 8 || tk > 0x7fffffffLL - 8) return MEA_EINVAL;
+  p.n_qtiles = (int)qt;
+  p.total_wg_q = (int)tq;
+  p.wg_per_xcd_q = (int)((tq + 7) / 8);
+  p.n_ktiles = (int)kt;
+  p.total_wg_k = (int)tk;
+  p.wg_per_xcd_k = (int)((tk + 7) / 8);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mea_debug() && varlen) {
+    int rc = debug_check_seqstart(seqstart_q, B, M, st);
+    if (rc == MEA_OK && seqstart_k != nullptr) rc = debug_check_seqstart(seqstart_k, B, N, st);
+    if (rc != MEA_OK) return rc;
+  }
+  return mea::launch_bwd(dtype, D, p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
 }
 
 size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {

@@ -1,0 +1,557 @@
+// Tiled exact attention backward pass for gfx950 (MI355X).
+//
+// Method: the score matrix is recomputed block by block from q, k and the
+// row log-sum-exp the forward stored, never read back from memory ("FlashAttention
+// (2022): l'attenzione che non satura la memoria", paithon.it, section on the
+// softmax that needs not see the whole row: the backward recomputes the scores
+// on the fly instead of keeping them). With P = exp(s - lse) the gradients are
+// the derivative of softmax(s) v, written with the softmax Jacobian:
+//   dP = dO V^T,   dS = P * (dP - Delta),   Delta_i = sum_d dO_id O_id,
+//   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+//
+// Three kernels, no atomics (every output element has a single writer, so
+// the result is deterministic):
+//   * bwd_prep_kernel: Delta and lse * log2(e) per (row, query head) into the
+//     caller's workspace (+inf for a row with no allowed key, so its P is 0);
+//   * bwd_dq_kernel: the forward's shape. A work-group owns 128 query rows of
+//     one (segment, query head), keeps Q and dO in registers and streams K/V
+//     blocks of 64 keys through LDS. S^T = K Q^T and dP^T = V dO^T leave one
+//     query per lane, so lse and Delta are per-lane scalars; dS^T is rounded
+//     to the input type and fed as the B operand of dQ^T += K^T dS^T, with K^T
+//     read from the row-major K block by ds_read_b64_tr_b16;
+//   * bwd_dkdv_kernel: the mirror image. A work-group owns 128 keys of one
+//     (segment, KV head) (32 per wave, K and V in registers) and streams
+//     64-query blocks of Q, dO, lse and Delta through LDS, for every query
+//     head that shares the KV head (grouped-query attention sums over them
+//     inside the work-group). S = Q K^T and dP = dO V^T leave one key per
+//     lane; P and dS, rounded, are the B operands of dV^T += dO^T P and
+//     dK^T += Q^T dS, with dO^T and Q^T from transpose reads.
+// Masks (causal bottom-right, segment ends) and ALiBi come from indices as in
+// the forward; blocks entirely above the diagonal are skipped.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mea {
+
+namespace {
+
+constexpr int kWaves = 4;
+// Waves per SIMD the register budget is tuned for: two at D=64; at D=128 the
+// resident K, V and both accumulators need the whole register file of one.
+template <int D>
+constexpr int kBwdWpe = D == 64 ? 2 : 1;
+
+template <typename T>
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  typedef T T2 __attribute__((ext_vector_type(2)));
+  const T2* x = reinterpret_cast<const T2*>(&a);
+  const T2* y = reinterpret_cast<const T2*>(&b);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (__is_same(T, __bf16))
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x[i], y[i], acc, false);
+    else
+      acc = __builtin_amdgcn_fdot2(x[i], y[i], acc, false);
+  }
+  return acc;
+}
+
+// ---- Delta and lse in log2 units --------------------------------------------
+// D/8 lanes per (row, head): each loads 16 bytes of O and dO.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
+  constexpr int CPR = D / 8;
+  constexpr int IPB = 256 / CPR;   // items per block per sweep
+  const int sub = threadIdx.x % CPR;
+  const long long n_items = p.rows * p.Hq;
+  for (long long item = (long long)blockIdx.x * IPB + threadIdx.x / CPR; item < n_items;
+       item += (long long)gridDim.x * IPB) {
+    const long long row = item / p.Hq;
+    const int h = (int)(item - row * p.Hq);
+    const long long e = row * p.q_rstride + (long long)h * D + sub * 8;
+    float acc = dot8<T>(*reinterpret_cast<const uint4*>(p.out + e), *reinterpret_cast<const uint4*>(p.dout + e));
+#pragma unroll
+    for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (sub == 0) {
+      const long long b = row / p.M;
+      const long long i = row - b * p.M;
+      const long long idx = (b * p.Hq + h) * p.M + i;
+      const float l = p.lse[idx];
+      p.delta[idx] = acc;
+      p.lse2[idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    }
+  }
+}
+
+// Segment of a packed batch holding logical tile t, with tiles of `bt` rows
+// counted over the boundaries in `st` (clamped to [0, total]). Returns the
+// segment index (B if t is past the last tile) and the tile's rank in it.
+__device__ __forceinline__ int find_tile(const int32_t* st, int B, int total, int bt, int t, int& rank, int& a0,
+                                         int& a1, int& ntile) {
+  int acc = 0, s = 0;
+  for (; s < B; ++s) {
+    a0 = min(max(st[s], 0), total);
+    a1 = min(max(st[s + 1], a0), total);
+    ntile = (a1 - a0 + bt - 1) / bt;
+    if (t < acc + ntile) break;
+    acc += ntile;
+  }
+  rank = t - acc;
+  return s;
+}
+
+// ---- dQ ------------------------------------------------------------------------
+template <typename T, int D, int CS, int AL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWpe<D>, kBwdWpe<D>))) bwd_dq_kernel(const BwdParams p) {
+  using MF = Mfma<T>;
+  typedef typename MF::v8 v8;
+  const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
+  const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
+  constexpr int QW = 32, BM = kWaves * QW, BN = 64;
+  constexpr int LDK = D + 8;             // row stride of the K and V blocks in LDS (elements)
+  constexpr int TILE = BN * LDK;
+  constexpr int CPR = D / 8, NLD = BN * CPR / (kWaves * 64);
+  constexpr int DB = D / 32, DS = D / 16;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int pid = blockIdx.x;
+  const int lid = (pid & 7) * p.wg_per_xcd_q + (pid >> 3);
+  if (lid >= p.total_wg_q) return;
+  const int bh = lid / p.n_qtiles;
+  const int t = lid - bh * p.n_qtiles;
+  const int h = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int g = h / p.group;
+
+  int M_s, N_s, tile;
+  long long qoff, koff, st_off;
+  if (!p.varlen) {
+    M_s = p.M;
+    N_s = p.N;
+    tile = CAUSAL ? (p.n_qtiles - 1 - t) : t;
+    qoff = (long long)b * p.q_bstride + (long long)h * D;
+    koff = (long long)b * p.kv_bstride + (long long)g * D;
+    st_off = ((long long)b * p.Hq + h) * p.M;
+  } else {
+    int rank, a0 = 0, a1 = 0, ntile = 0;
+    const int s = find_tile(p.seqstart_q, p.B, p.M, BM, t, rank, a0, a1, ntile);
+    if (s >= p.B) return;
+    tile = CAUSAL ? (ntile - 1 - rank) : rank;
+    const int k0 = min(max(p.seqstart_k[s], 0), p.N);
+    const int k1 = min(max(p.seqstart_k[s + 1], k0), p.N);
+    M_s = a1 - a0;
+    N_s = k1 - k0;
+    qoff = (long long)a0 * p.q_rstride + (long long)h * D;
+    koff = (long long)k0 * p.kv_rstride + (long long)g * D;
+    st_off = (long long)h * p.M + a0;
+  }
+
+  const int i0 = tile * BM;
+  const int off = N_s - M_s;
+  int kend = N_s;
+  if (CAUSAL) kend = min(N_s, i0 + BM + off);
+  kend = max(kend, 0);
+  const int ntiles = (kend + BN - 1) / BN;
+
+  const int wq0 = i0 + wave * QW;
+  const int wlast = min(wq0 + QW, M_s) - 1;
+  int wkend = 0;
+  if (wlast >= wq0) wkend = CAUSAL ? max(min(N_s, wlast + off + 1), 0) : N_s;
+
+  const float c = p.scale_log2;
+  const float slope = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+  const int qi = wq0 + l32;
+  const bool qin = qi < M_s;
+  const float lse2 = qin ? p.lse2[st_off + qi] : INFINITY;
+  const float dlt = qin ? p.delta[st_off + qi] : 0.f;
+
+  v8 qf[DS], df[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) {
+    const long long e = qoff + (long long)qi * p.q_rstride + st * 16 + hi * 8;
+    qf[st] = qin ? load_v8<T>(p.q + e) : zero_v8<T>();
+    df[st] = qin ? load_v8<T>(p.dout + e) : zero_v8<T>();
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  uint4 kst[NLD], vst[NLD];
+  const uint32_t row_bytes = (uint32_t)p.kv_rstride * 2u;
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int ch = tid + i * (kWaves * 64);
+    const int r = ch / CPR;
+    ld_off[i] = (uint32_t)r * row_bytes + (uint32_t)(ch - r * CPR) * 16u;
+  }
+  auto gload = [&](int kt) {
+    const uint32_t bytes = rows_bytes(N_s - kt * BN, row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + koff + (long long)kt * BN * p.kv_rstride, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + koff + (long long)kt * BN * p.kv_rstride, bytes);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      kst[i] = buf_load16(rk, ld_off[i]);
+      vst[i] = buf_load16(rv, ld_off[i]);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* ks = smem + buf * 2 * TILE;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int ch = tid + i * (kWaves * 64);
+      const int r = ch / CPR;
+      const int cc = (ch - r * CPR) * 8;
+      *reinterpret_cast<uint4*>(ks + r * LDK + cc) = kst[i];
+      *reinterpret_cast<uint4*>(ks + TILE + r * LDK + cc) = vst[i];
+    }
+  };
+
+  const int g16 = lane >> 4;
+  const int ll = lane & 15;
+  const int trow = (g16 >> 1) * 4 + (ll >> 2);
+  const int tcol = (g16 & 1) * 16 + 4 * (ll & 3);
+
+  if (ntiles > 0) gload(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    lstore(buf);
+    __syncthreads();
+    if (kt + 1 < ntiles) gload(kt + 1);
+
+    const int key_base = kt * BN;
+    if (key_base >= wkend) continue;
+    const uint16_t* Ks = smem + buf * 2 * TILE;
+    const uint16_t* Vs = Ks + TILE;
+
+    // S^T = K Q^T and dP^T = V dO^T (one query per lane, 32 keys per block)
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = 0.f;
+        dp[kb][r] = 0.f;
+      }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        s[kb] = MF::mma32(load_v8<T>(Ks + (kb * 32 + l32) * LDK + st * 16 + hi * 8), qf[st], s[kb]);
+        dp[kb] = MF::mma32(load_v8<T>(Vs + (kb * 32 + l32) * LDK + st * 16 + hi * 8), df[st], dp[kb]);
+      }
+    __builtin_amdgcn_s_setprio(0);
+
+    // P = 2^(s c + bias - lse2), dS = P (dP - Delta), rounded to T.
+    const bool need_mask = (key_base + BN > N_s) || (CAUSAL && key_base + BN - 1 > wq0 + off);
+    const int rel = key_base + hi * 4;
+    const int lim_n = N_s - rel;
+    const int lim_c = CAUSAL ? (qi + off - rel) : 0x7fffffff;
+    const float dist0 = (float)(qi + off - rel);
+    v8 dsf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
+        float x = fmaf(s[kb][r], c, -lse2);
+        if (ALIBI) x -= slope * fabsf(dist0 - (float)kr);
+        if (need_mask) x = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
+        const float pr = fast_exp2(x);
+        dsf[kb * 2 + (r >> 3)][r & 7] = (T)(pr * (dp[kb][r] - dlt));
+      }
+
+    // dQ^T += K^T dS^T
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const uint16_t* a0 = Ks + (tt * 16 + trow) * LDK + db * 32 + tcol;
+        acc[db] = MF::mma32(lds_tr_x8<T>(a0, a0 + 8 * LDK), dsf[tt], acc[db]);
+      }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  if (qin) {
+    uint16_t* orow = p.dq + qoff + (long long)qi * p.q_rstride;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        typename MF::v4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = (T)(acc[db][rg * 4 + u] * p.scale);
+        *reinterpret_cast<uint2*>(orow + db * 32 + rg * 8 + hi * 4) = __builtin_bit_cast(uint2, w);
+      }
+  }
+}
+
+// ---- dK, dV ----------------------------------------------------------------------
+template <typename T, int D, int CS, int AL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWpe<D>, kBwdWpe<D>))) bwd_dkdv_kernel(const BwdParams p) {
+  using MF = Mfma<T>;
+  typedef typename MF::v8 v8;
+  const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
+  const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
+  constexpr int KW = 32, BNK = kWaves * KW, BQ = 64;
+  constexpr int LDQ = D + 8;             // row stride of the Q and dO blocks in LDS (elements)
+  constexpr int TILE = BQ * LDQ;
+  constexpr int CPR = D / 8, NLD = BQ * CPR / (kWaves * 64);
+  constexpr int DB = D / 32, DS = D / 16;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float sstat[2][2][BQ];   // [buf][lse2, Delta][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int pid = blockIdx.x;
+  const int lid = (pid & 7) * p.wg_per_xcd_k + (pid >> 3);
+  if (lid >= p.total_wg_k) return;
+  const int bg = lid / p.n_ktiles;
+  const int t = lid - bg * p.n_ktiles;
+  const int g = bg % p.Hkv;
+  const int b = bg / p.Hkv;
+
+  int M_s, N_s, tile;
+  long long qbase, koff, st_base;   // qbase: row 0 of the segment, head 0
+  if (!p.varlen) {
+    M_s = p.M;
+    N_s = p.N;
+    tile = t;
+    qbase = (long long)b * p.q_bstride;
+    koff = (long long)b * p.kv_bstride + (long long)g * D;
+    st_base = (long long)b * p.Hq * p.M;
+  } else {
+    int rank, a0 = 0, a1 = 0, ntile = 0;
+    const int s = find_tile(p.seqstart_k, p.B, p.N, BNK, t, rank, a0, a1, ntile);
+    if (s >= p.B) return;
+    tile = rank;
+    const int q0 = min(max(p.seqstart_q[s], 0), p.M);
+    const int q1 = min(max(p.seqstart_q[s + 1], q0), p.M);
+    M_s = q1 - q0;
+    N_s = a1 - a0;
+    qbase = (long long)q0 * p.q_rstride;
+    koff = (long long)a0 * p.kv_rstride + (long long)g * D;
+    st_base = q0;
+  }
+  // Statistics are [B][Hq][M] (packed: [Hq][M]); one head spans M rows.
+  const float c = p.scale_log2;
+  const int off = N_s - M_s;
+  const int j0 = tile * BNK;
+  const int wj0 = j0 + wave * KW;        // first key of this wave
+  const int kj = wj0 + l32;              // this lane's key
+  const bool kin = kj < N_s;
+
+  // Queries that can see keys >= j0: i >= j0 - off under the causal mask.
+  int qfirst = 0;
+  if (CAUSAL) qfirst = max(j0 - off, 0);
+  qfirst = (qfirst / BQ) * BQ;
+  const int nqt = M_s > qfirst ? (M_s - qfirst + BQ - 1) / BQ : 0;
+  const int niter = nqt * p.group;
+
+  v8 kf[DS], vf[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) {
+    const long long e = koff + (long long)kj * p.kv_rstride + st * 16 + hi * 8;
+    kf[st] = kin ? load_v8<T>(p.k + e) : zero_v8<T>();
+    vf[st] = kin ? load_v8<T>(p.v + e) : zero_v8<T>();
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dka[db][r] = 0.f;
+      dva[db][r] = 0.f;
+    }
+
+  uint4 qst[NLD], dst[NLD];
+  float stv = 0.f;
+  const uint32_t row_bytes = (uint32_t)p.q_rstride * 2u;
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int ch = tid + i * (kWaves * 64);
+    const int r = ch / CPR;
+    ld_off[i] = (uint32_t)r * row_bytes + (uint32_t)(ch - r * CPR) * 16u;
+  }
+  auto gload = [&](int it) {
+    const int hh = it / nqt;
+    const int qt = it - hh * nqt;
+    const int h = g * p.group + hh;
+    const int r0 = qfirst + qt * BQ;
+    const uint32_t bytes = rows_bytes(M_s - r0, row_bytes);
+    const long long base = qbase + (long long)r0 * p.q_rstride + (long long)h * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dout + base, bytes);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      qst[i] = buf_load16(rq, ld_off[i]);
+      dst[i] = buf_load16(rd, ld_off[i]);
+    }
+    if (tid < 2 * BQ) {
+      const int r = tid & (BQ - 1);
+      const long long si = st_base + (long long)h * p.M + r0 + r;
+      const bool in = r0 + r < M_s;
+      stv = tid < BQ ? (in ? p.lse2[si] : INFINITY) : (in ? p.delta[si] : 0.f);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* qs = smem + buf * 2 * TILE;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int ch = tid + i * (kWaves * 64);
+      const int r = ch / CPR;
+      const int cc = (ch - r * CPR) * 8;
+      *reinterpret_cast<uint4*>(qs + r * LDQ + cc) = qst[i];
+      *reinterpret_cast<uint4*>(qs + TILE + r * LDQ + cc) = dst[i];
+    }
+    if (tid < 2 * BQ) sstat[buf][tid >> 6][tid & (BQ - 1)] = stv;
+  };
+
+  const int g16 = lane >> 4;
+  const int ll = lane & 15;
+  const int trow = (g16 >> 1) * 4 + (ll >> 2);
+  const int tcol = (g16 & 1) * 16 + 4 * (ll & 3);
+  const bool wave_has_keys = wj0 < N_s;
+
+  if (niter > 0) gload(0);
+  for (int it = 0; it < niter; ++it) {
+    const int buf = it & 1;
+    lstore(buf);
+    __syncthreads();
+    const int hh = it / nqt;
+    const int qt = it - hh * nqt;
+    if (it + 1 < niter) gload(it + 1);
+    if (!wave_has_keys) continue;
+
+    const int h = g * p.group + hh;
+    const float slope = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const uint16_t* Qs = smem + buf * 2 * TILE;
+    const uint16_t* Os = Qs + TILE;
+    const int r0 = qfirst + qt * BQ;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qb0 = r0 + qs * 32;      // first query of this 32-row block
+      // Under the causal mask the block's last query sees keys <= qb0 + 31 + off.
+      if (CAUSAL && qb0 + 31 + off < wj0) continue;
+      if (qb0 >= M_s) continue;
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        s = MF::mma32(load_v8<T>(Qs + (qs * 32 + l32) * LDQ + st * 16 + hi * 8), kf[st], s);
+        dp = MF::mma32(load_v8<T>(Os + (qs * 32 + l32) * LDQ + st * 16 + hi * 8), vf[st], dp);
+      }
+      __builtin_amdgcn_s_setprio(0);
+
+      // This lane's key kj; its 16 queries qb0 + rg*8 + hi*4 + u (r = rg*4 + u).
+      const bool need_mask = CAUSAL && (qb0 + off < wj0 + KW - 1);
+      v8 pf[2], dsf[2];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int rr = qs * 32 + rg * 8 + hi * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sstat[buf][0][rr]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sstat[buf][1][rr]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = rg * 4 + u;
+          const int qpos = qb0 + rg * 8 + hi * 4 + u + off;   // query position - key = qpos - kj
+          float x = fmaf(s[r], c, -l4[u]);
+          if (ALIBI) x -= slope * fabsf((float)(qpos - kj));
+          if (need_mask) x = (kj <= qpos) ? x : -INFINITY;
+          const float pr = fast_exp2(x);
+          pf[r >> 3][r & 7] = (T)pr;
+          dsf[r >> 3][r & 7] = (T)(pr * (dp[r] - d4[u]));
+        }
+      }
+
+      // dV^T += dO^T P,  dK^T += Q^T dS
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int ro = (qs * 32 + tt * 16 + trow) * LDQ + db * 32 + tcol;
+          dva[db] = MF::mma32(lds_tr_x8<T>(Os + ro, Os + ro + 8 * LDQ), pf[tt], dva[db]);
+          dka[db] = MF::mma32(lds_tr_x8<T>(Qs + ro, Qs + ro + 8 * LDQ), dsf[tt], dka[db]);
+        }
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+
+  if (kin) {
+    const long long e = koff + (long long)kj * p.kv_rstride;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        typename MF::v4 wk, wv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wk[u] = (T)(dka[db][rg * 4 + u] * p.scale);
+          wv[u] = (T)dva[db][rg * 4 + u];
+        }
+        const int col = db * 32 + rg * 8 + hi * 4;
+        *reinterpret_cast<uint2*>(p.dk + e + col) = __builtin_bit_cast(uint2, wk);
+        *reinterpret_cast<uint2*>(p.dv + e + col) = __builtin_bit_cast(uint2, wv);
+      }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
+  {
+    constexpr int IPB = 256 / (D / 8);
+    const long long items = p.rows * p.Hq;
+    long long blocks = (items + IPB - 1) / IPB;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks > 0) hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  }
+  const dim3 gq(p.wg_per_xcd_q * 8), gk(p.wg_per_xcd_k * 8), blk(kWaves * 64);
+  if (!p.causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 0, 2>), gk, blk, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, 0, 2>), gq, blk, 0, stream, p);
+  } else if (p.alibi) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 1, 1>), gk, blk, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, 1, 1>), gq, blk, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 1, 0>), gk, blk, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, 1, 0>), gq, blk, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dtype(int D, const BwdParams& p, hipStream_t stream) {
+  return D == 64 ? launch_typed<T, 64>(p, stream) : launch_typed<T, 128>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int dtype, int D, const BwdParams& p, hipStream_t stream) {
+  return dtype == 0 ? launch_dtype<_Float16>(D, p, stream) : launch_dtype<__bf16>(D, p, stream);
+}
+
+}  // namespace mea

@@ -42,6 +42,34 @@ struct DecParams {
   float scale_log2;
 };
 
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;      // natural log, [B][Hq][M] (packed: [Hq][M])
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* lse2;           // workspace: lse * log2(e), +inf for rows with no key; layout of lse
+  float* delta;          // workspace: rowsum(dO * O); layout of lse
+  const int32_t* seqstart_q;
+  const int32_t* seqstart_k;
+  const float* slopes;
+  int B, M, N, Hq, Hkv, group;
+  int causal, varlen, alibi;
+  float scale;           // as given
+  float scale_log2;      // scale * log2(e)
+  long long rows;        // query rows over all batch entries (dense B*M, packed M)
+  int n_qtiles, total_wg_q, wg_per_xcd_q;   // dQ kernel: 128-row query tiles
+  int n_ktiles, total_wg_k, wg_per_xcd_k;   // dK/dV kernel: 128-key tiles
+  long long q_bstride;
+  long long kv_bstride;
+  int q_rstride;
+  int kv_rstride;
+};
+
 // Query rows per forward work-group and the decode chunk length.
 int fwd_block_m(int D, bool causal);
 constexpr int kDecodeChunk = 512;
@@ -58,5 +86,8 @@ struct AppendParams {
 hipError_t launch_fwd(int dtype, int D, const FwdParams& p, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(int dtype, int D, const DecParams& p, hipStream_t stream);
+hipError_t launch_bwd(int dtype, int D, const BwdParams& p, hipStream_t stream);
+constexpr int kBwdTileQ = 128;   // query rows per dQ work-group
+constexpr int kBwdTileK = 128;   // keys per dK/dV work-group
 
 }  // namespace mea
