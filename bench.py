@@ -10,6 +10,9 @@ input already resident in HBM:
      Hkv=8, D=128, bf16, block-diagonal causal mask + ALiBi
   4. decode step, B=32, contexts uniform in [1024, 32768], Hq=32, Hkv=8,
      D=128, bf16 KV cache of 32768 slots per sequence
+  5. backward (dq, dk, dv) of items 1 and 2, from their stored output and
+     lse and a seeded upstream gradient (10*D algorithmic flops per allowed
+     query-key pair: S recomputed, dP, dV, dK, dQ)
 
 Prints ONE JSON line on stdout. ``value`` is the headline forward throughput
 (algorithmic TFLOP/s of item 1: 4*B*H*M*N*D flops over its average launch
@@ -229,7 +232,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode",
+    ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode,bwd_noncausal,bwd_causal",
                     help="comma-separated subset of the step to run (for profiling one kernel)")
     ap.add_argument("--table", action="store_true",
                     help="reproduce the tutorial's naive-vs-memory-efficient table (ms, peak MB) for seqlen 512..4096")
@@ -268,6 +271,20 @@ def main():
     out_c = torch.empty_like(d["q"])
     out_v = torch.empty_like(vl["q"])
     out_dec = torch.empty_like(dc["q"])
+    # Backward inputs: the forward's output and lse (computed once, untimed)
+    # and a seeded upstream gradient.
+    B_, M_, H_ = d["q"].shape[:3]
+    dout = to_dev(inp.normal_bits(7, tuple(d["q"].shape), "bf16", 0), torch)
+    fb = {}
+    for cz in (False, True):
+        lse_ = torch.empty((B_, H_, M_), dtype=torch.float32, device="cuda")
+        o_ = mea.fwd(d["q"], d["k"], d["v"], causal=cz, lse=lse_)
+        fb[cz] = (o_, lse_, torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
+                  torch.empty(mea.bwd_workspace_bytes(B_, M_, H_, int(cz)), dtype=torch.uint8, device="cuda"))
+
+    def bwd_item(cz):
+        o_, lse_, gq, gk, gv, wsb = fb[cz]
+        return lambda: mea.bwd(d["q"], d["k"], d["v"], o_, dout, lse_, causal=cz, dq=gq, dk=gk, dv=gv, workspace=wsb)
 
     items = [
         ("fwd_noncausal", lambda: mea.fwd(d["q"], d["k"], d["v"], out=out_d)),
@@ -275,6 +292,8 @@ def main():
         ("fwd_varlen", lambda: mea.fwd(vl["q"], vl["k"], vl["v"], causal=True, seqstart_q=vl["seqstart"],
                                        alibi_slopes=vl["slopes"], out=out_v)),
         ("decode", lambda: mea.decode(dc["q"], dc["kc"], dc["vc"], dc["ctx"], out=out_dec, workspace=ws)),
+        ("bwd_noncausal", bwd_item(False)),
+        ("bwd_causal", bwd_item(True)),
     ]
     wanted = set(args.items.split(","))
     unknown = wanted - {n for n, _ in items}
@@ -312,6 +331,8 @@ def main():
         "fwd_noncausal": 4.0 * 4 * 16 * 4096 * 4096 * 64,
         "fwd_causal": 4.0 * 4 * 16 * 64 * (4096 * 4097 / 2),
         "fwd_varlen": 4.0 * 128 * 32 * float(np.sum(L * (L + 1) // 2)),
+        "bwd_noncausal": 10.0 * 4 * 16 * 4096 * 4096 * 64,
+        "bwd_causal": 10.0 * 4 * 16 * 64 * (4096 * 4097 / 2),
     }
     ctx = x["decode"]["ctx_host"].astype(np.int64)
     dec_bytes = float(ctx.sum() * 8 * 128 * 2 * 2 + 32 * 32 * 128 * 2 * 2)
@@ -347,7 +368,8 @@ def main():
         "config": {
             "workload": "attention forward B=4 M=N=4096 H=16 D=64 bf16 (no mask; causal beside it) "
                         "+ packed 8x[64,2048] Hq=32 Hkv=8 D=128 block-diag causal ALiBi "
-                        "+ decode B=32 ctx[1024,32768] Hq=32 Hkv=8 D=128",
+                        "+ decode B=32 ctx[1024,32768] Hq=32 Hkv=8 D=128 "
+                        "+ backward of the two B=4 M=4096 forwards",
             "items": sorted(ms),
             "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)",
         },
@@ -365,6 +387,13 @@ def main():
             "traffic": traffic_for(traffic, "decode_split_kernelIDF16bLi128", "decode_combine_kernelIDF16bLi128"),
             "kernel": "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
             "avg_launch_us": round(ms["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes,
+        },
+        "roofline_bwd": None if "bwd_noncausal" not in tflops else {
+            "bound": "mfma", "achieved": round(tflops["bwd_noncausal"], 2), "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops["bwd_noncausal"] / PEAK_MFMA_TFLOPS, 4),
+            "kernel": "bwd_prep + bwd_dkdv + bwd_dq <bf16,64> (non-causal)",
+            "avg_launch_us": round(ms["bwd_noncausal"] * 1e3, 2),
+            "algorithmic_flops": flops_all["bwd_noncausal"],
         },
         "per_item": per_item,
         "cpu_baseline": None,

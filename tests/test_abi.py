@@ -102,6 +102,45 @@ def test_decode_rejects(kw, status):
     assert _dec(**kw) == status
 
 
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=2, M=64, N=80, Hq=4,
+             Hkv=2, D=64, scale=0.125, kind=mea.MEA_MASK_CAUSAL, sq=None, sk=None, sl=None, dtype=mea.MEA_BF16,
+             ws=ctypes.c_void_p(0x100000), wsb=1 << 20, stream=None)
+    a.update(kw)
+    return mea.lib().mea_bwd(a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                             a["B"], a["M"], a["N"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["kind"], a["sq"],
+                             a["sk"], a["sl"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), mea.MEA_EINVAL),
+    (dict(out=None), mea.MEA_EINVAL),
+    (dict(do=None), mea.MEA_EINVAL),
+    (dict(dk=None), mea.MEA_EINVAL),
+    (dict(N=0), mea.MEA_EINVAL),
+    (dict(Hq=3), mea.MEA_EINVAL),
+    (dict(scale=float("nan")), mea.MEA_EINVAL),
+    (dict(kind=16), mea.MEA_EINVAL),
+    (dict(kind=mea.MEA_BIAS_ALIBI), mea.MEA_EINVAL),
+    (dict(kind=mea.MEA_MASK_BLOCKDIAG), mea.MEA_EINVAL),
+    (dict(kind=mea.MEA_MASK_BLOCKDIAG, sq=FAKE), mea.MEA_EINVAL),   # M != N needs seqstart_k
+    (dict(D=256), mea.MEA_EUNSUPPORTED),
+    (dict(ws=None), mea.MEA_EWORKSPACE),
+    (dict(wsb=1024), mea.MEA_EWORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100040)), mea.MEA_EWORKSPACE),
+])
+def test_bwd_rejects(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    one = ((2 * 64 * 4 * 4 + 255) // 256) * 256
+    assert mea.bwd_workspace_bytes(2, 64, 4, mea.MEA_MASK_CAUSAL) == 2 * one
+    packed = ((64 * 4 * 4 + 255) // 256) * 256          # packed: one physical batch row
+    assert mea.bwd_workspace_bytes(2, 64, 4, mea.MEA_MASK_BLOCKDIAG) == 2 * packed
+    assert mea.bwd_workspace_bytes(0, 64, 4, 0) == 0
+
+
 def test_product_package_does_not_reach_the_oracle():
     """The product package neither imports nor names the oracle."""
     pkg = os.path.join(ROOT, "memory_efficient_exact_tiled_amd")
