@@ -109,8 +109,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
   const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
   constexpr int QW = 32, BM = kWaves * QW, BN = 64;
-  constexpr int LDK = D + 8;             // row stride of the K and V blocks in LDS (elements)
-  constexpr int TILE = BN * LDK;
+  constexpr int TILE = BN * D;           // K and V blocks in LDS, swizzled (swz)
   constexpr int CPR = D / 8, NLD = BN * CPR / (kWaves * 64);
   constexpr int DB = D / 32, DS = D / 16;
 
@@ -118,7 +117,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: masks branch, not select
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -212,8 +211,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       const int ch = tid + i * (kWaves * 64);
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(ks + r * LDK + cc) = kst[i];
-      *reinterpret_cast<uint4*>(ks + TILE + r * LDK + cc) = vst[i];
+      *reinterpret_cast<uint4*>(ks + swz<D>(r, cc)) = kst[i];
+      *reinterpret_cast<uint4*>(ks + TILE + swz<D>(r, cc)) = vst[i];
     }
   };
 
@@ -248,29 +247,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        s[kb] = MF::mma32(load_v8<T>(Ks + (kb * 32 + l32) * LDK + st * 16 + hi * 8), qf[st], s[kb]);
-        dp[kb] = MF::mma32(load_v8<T>(Vs + (kb * 32 + l32) * LDK + st * 16 + hi * 8), df[st], dp[kb]);
+        const int a = swz<D>(kb * 32 + l32, st * 16 + hi * 8);
+        s[kb] = MF::mma32(load_v8<T>(Ks + a), qf[st], s[kb]);
+        dp[kb] = MF::mma32(load_v8<T>(Vs + a), df[st], dp[kb]);
       }
     __builtin_amdgcn_s_setprio(0);
 
-    // P = 2^(s c + bias - lse2), dS = P (dP - Delta), rounded to T.
+    // P = 2^(s c + bias - lse2), dS = P (dP - Delta), rounded to T. The
+    // exponent is formed in s: explicitly (bias, mask) only on blocks that
+    // need it.
     const bool need_mask = (key_base + BN > N_s) || (CAUSAL && key_base + BN - 1 > wq0 + off);
-    const int rel = key_base + hi * 4;
-    const int lim_n = N_s - rel;
-    const int lim_c = CAUSAL ? (qi + off - rel) : 0x7fffffff;
-    const float dist0 = (float)(qi + off - rel);
+    if (ALIBI || need_mask) {
+      const int rel = key_base + hi * 4;
+      const int lim_n = N_s - rel;
+      const int lim_c = CAUSAL ? (qi + off - rel) : 0x7fffffff;
+      const float dist0 = (float)(qi + off - rel);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
+          float x = fmaf(s[kb][r], c, -lse2);
+          if (ALIBI) x -= slope * fabsf(dist0 - (float)kr);
+          s[kb][r] = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -lse2);
+    }
     v8 dsf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
-        float x = fmaf(s[kb][r], c, -lse2);
-        if (ALIBI) x -= slope * fabsf(dist0 - (float)kr);
-        if (need_mask) x = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
-        const float pr = fast_exp2(x);
-        dsf[kb * 2 + (r >> 3)][r & 7] = (T)(pr * (dp[kb][r] - dlt));
-      }
+      for (int r = 0; r < 16; ++r)
+        dsf[kb * 2 + (r >> 3)][r & 7] = (T)(fast_exp2(s[kb][r]) * (dp[kb][r] - dlt));
 
     // dQ^T += K^T dS^T
     __builtin_amdgcn_s_setprio(1);
@@ -278,8 +290,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const uint16_t* a0 = Ks + (tt * 16 + trow) * LDK + db * 32 + tcol;
-        acc[db] = MF::mma32(lds_tr_x8<T>(a0, a0 + 8 * LDK), dsf[tt], acc[db]);
+        const int c0 = db * 32 + tcol;
+        acc[db] = MF::mma32(lds_tr_x8<T>(Ks + swz<D>(tt * 16 + trow, c0), Ks + swz<D>(tt * 16 + trow + 8, c0)),
+                            dsf[tt], acc[db]);
       }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -306,8 +319,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
   const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
   constexpr int KW = 32, BNK = kWaves * KW, BQ = 64;
-  constexpr int LDQ = D + 8;             // row stride of the Q and dO blocks in LDS (elements)
-  constexpr int TILE = BQ * LDQ;
+  constexpr int TILE = BQ * D;           // Q and dO blocks in LDS, swizzled (swz)
   constexpr int CPR = D / 8, NLD = BQ * CPR / (kWaves * 64);
   constexpr int DB = D / 32, DS = D / 16;
 
@@ -316,7 +328,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: masks branch, not select
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -419,8 +431,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       const int ch = tid + i * (kWaves * 64);
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(qs + r * LDQ + cc) = qst[i];
-      *reinterpret_cast<uint4*>(qs + TILE + r * LDQ + cc) = dst[i];
+      *reinterpret_cast<uint4*>(qs + swz<D>(r, cc)) = qst[i];
+      *reinterpret_cast<uint4*>(qs + TILE + swz<D>(r, cc)) = dst[i];
     }
     if (tid < 2 * BQ) sstat[buf][tid >> 6][tid & (BQ - 1)] = stv;
   };
@@ -461,30 +473,40 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        s = MF::mma32(load_v8<T>(Qs + (qs * 32 + l32) * LDQ + st * 16 + hi * 8), kf[st], s);
-        dp = MF::mma32(load_v8<T>(Os + (qs * 32 + l32) * LDQ + st * 16 + hi * 8), vf[st], dp);
+        const int a = swz<D>(qs * 32 + l32, st * 16 + hi * 8);
+        s = MF::mma32(load_v8<T>(Qs + a), kf[st], s);
+        dp = MF::mma32(load_v8<T>(Os + a), vf[st], dp);
       }
       __builtin_amdgcn_s_setprio(0);
 
       // This lane's key kj; its 16 queries qb0 + rg*8 + hi*4 + u (r = rg*4 + u).
+      // The exponent s c + bias - lse2 is formed in s; bias and mask only on
+      // blocks that need them.
       const bool need_mask = CAUSAL && (qb0 + off < wj0 + KW - 1);
-      v8 pf[2], dsf[2];
+      f32x4 d4[4];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int rr = qs * 32 + rg * 8 + hi * 4;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sstat[buf][0][rr]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sstat[buf][1][rr]);
+        d4[rg] = *reinterpret_cast<const f32x4*>(&sstat[buf][1][rr]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = rg * 4 + u;
-          const int qpos = qb0 + rg * 8 + hi * 4 + u + off;   // query position - key = qpos - kj
-          float x = fmaf(s[r], c, -l4[u]);
-          if (ALIBI) x -= slope * fabsf((float)(qpos - kj));
-          if (need_mask) x = (kj <= qpos) ? x : -INFINITY;
-          const float pr = fast_exp2(x);
-          pf[r >> 3][r & 7] = (T)pr;
-          dsf[r >> 3][r & 7] = (T)(pr * (dp[r] - d4[u]));
+        for (int u = 0; u < 4; ++u) s[rg * 4 + u] = fmaf(s[rg * 4 + u], c, -l4[u]);
+      }
+      if (ALIBI || need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dist = qb0 + (r >> 2) * 8 + hi * 4 + (r & 3) + off - kj;   // query position - key
+          float x = s[r];
+          if (ALIBI) x -= slope * fabsf((float)dist);
+          s[r] = (!need_mask || dist >= 0) ? x : -INFINITY;
         }
+      }
+      v8 pf[2], dsf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = fast_exp2(s[r]);
+        pf[r >> 3][r & 7] = (T)pr;
+        dsf[r >> 3][r & 7] = (T)(pr * (dp[r] - d4[r >> 2][r & 3]));
       }
 
       // dV^T += dO^T P,  dK^T += Q^T dS
@@ -493,9 +515,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const int ro = (qs * 32 + tt * 16 + trow) * LDQ + db * 32 + tcol;
-          dva[db] = MF::mma32(lds_tr_x8<T>(Os + ro, Os + ro + 8 * LDQ), pf[tt], dva[db]);
-          dka[db] = MF::mma32(lds_tr_x8<T>(Qs + ro, Qs + ro + 8 * LDQ), dsf[tt], dka[db]);
+          const int r0 = qs * 32 + tt * 16 + trow, c0 = db * 32 + tcol;
+          const int a0 = swz<D>(r0, c0), a1 = swz<D>(r0 + 8, c0);
+          dva[db] = MF::mma32(lds_tr_x8<T>(Os + a0, Os + a1), pf[tt], dva[db]);
+          dka[db] = MF::mma32(lds_tr_x8<T>(Qs + a0, Qs + a1), dsf[tt], dka[db]);
         }
       __builtin_amdgcn_s_setprio(0);
     }
