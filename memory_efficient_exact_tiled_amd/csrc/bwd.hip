@@ -41,6 +41,16 @@ constexpr int kWaves = 4;
 template <int D>
 constexpr int kBwdWpe = D == 64 ? 2 : 1;
 
+// LDS tiles are row-major with rows padded to D + 8 elements: the 16-row
+// ds_read_b128 operand reads are then conflict-free; the transpose reads
+// conflict two ways on half their banks. An XOR swizzle of the 16-byte chunks
+// removes those conflicts too, but measured slower on both kernels: the extra
+// address arithmetic lands on the VALU, which bounds them.
+template <int D>
+__device__ __forceinline__ int lds_at(int row, int col) {
+  return row * (D + 8) + col;
+}
+
 template <typename T>
 __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   typedef T T2 __attribute__((ext_vector_type(2)));
@@ -109,7 +119,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
   const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
   constexpr int QW = 32, BM = kWaves * QW, BN = 64;
-  constexpr int TILE = BN * D;           // K and V blocks in LDS, swizzled (swz)
+  constexpr int TILE = BN * (D + 8);     // K and V blocks in LDS (lds_at)
   constexpr int CPR = D / 8, NLD = BN * CPR / (kWaves * 64);
   constexpr int DB = D / 32, DS = D / 16;
 
@@ -211,8 +221,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       const int ch = tid + i * (kWaves * 64);
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(ks + swz<D>(r, cc)) = kst[i];
-      *reinterpret_cast<uint4*>(ks + TILE + swz<D>(r, cc)) = vst[i];
+      *reinterpret_cast<uint4*>(ks + lds_at<D>(r, cc)) = kst[i];
+      *reinterpret_cast<uint4*>(ks + TILE + lds_at<D>(r, cc)) = vst[i];
     }
   };
 
@@ -247,7 +257,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        const int a = swz<D>(kb * 32 + l32, st * 16 + hi * 8);
+        const int a = lds_at<D>(kb * 32 + l32, st * 16 + hi * 8);
         s[kb] = MF::mma32(load_v8<T>(Ks + a), qf[st], s[kb]);
         dp[kb] = MF::mma32(load_v8<T>(Vs + a), df[st], dp[kb]);
       }
@@ -291,7 +301,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int c0 = db * 32 + tcol;
-        acc[db] = MF::mma32(lds_tr_x8<T>(Ks + swz<D>(tt * 16 + trow, c0), Ks + swz<D>(tt * 16 + trow + 8, c0)),
+        acc[db] = MF::mma32(lds_tr_x8<T>(Ks + lds_at<D>(tt * 16 + trow, c0), Ks + lds_at<D>(tt * 16 + trow + 8, c0)),
                             dsf[tt], acc[db]);
       }
     __builtin_amdgcn_s_setprio(0);
@@ -319,7 +329,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
   const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
   constexpr int KW = 32, BNK = kWaves * KW, BQ = 64;
-  constexpr int TILE = BQ * D;           // Q and dO blocks in LDS, swizzled (swz)
+  constexpr int TILE = BQ * (D + 8);     // Q and dO blocks in LDS (lds_at)
   constexpr int CPR = D / 8, NLD = BQ * CPR / (kWaves * 64);
   constexpr int DB = D / 32, DS = D / 16;
 
@@ -431,8 +441,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       const int ch = tid + i * (kWaves * 64);
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(qs + swz<D>(r, cc)) = qst[i];
-      *reinterpret_cast<uint4*>(qs + TILE + swz<D>(r, cc)) = dst[i];
+      *reinterpret_cast<uint4*>(qs + lds_at<D>(r, cc)) = qst[i];
+      *reinterpret_cast<uint4*>(qs + TILE + lds_at<D>(r, cc)) = dst[i];
     }
     if (tid < 2 * BQ) sstat[buf][tid >> 6][tid & (BQ - 1)] = stv;
   };
@@ -473,7 +483,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        const int a = swz<D>(qs * 32 + l32, st * 16 + hi * 8);
+        const int a = lds_at<D>(qs * 32 + l32, st * 16 + hi * 8);
         s = MF::mma32(load_v8<T>(Qs + a), kf[st], s);
         dp = MF::mma32(load_v8<T>(Os + a), vf[st], dp);
       }
@@ -516,7 +526,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int r0 = qs * 32 + tt * 16 + trow, c0 = db * 32 + tcol;
-          const int a0 = swz<D>(r0, c0), a1 = swz<D>(r0 + 8, c0);
+          const int a0 = lds_at<D>(r0, c0), a1 = lds_at<D>(r0 + 8, c0);
           dva[db] = MF::mma32(lds_tr_x8<T>(Os + a0, Os + a1), pf[tt], dva[db]);
           dka[db] = MF::mma32(lds_tr_x8<T>(Qs + a0, Qs + a1), dsf[tt], dka[db]);
         }

@@ -109,28 +109,6 @@ __device__ __forceinline__ uint32_t rows_bytes(long long n, long long row_bytes)
   return b > 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
 }
 
-// Element offset of (row, col) in an unpadded row-major LDS tile of D
-// 2-byte elements per row whose 16-byte chunks are XOR-swizzled by row:
-// chunk c of row r is stored at chunk c ^ f(r). f is a bit reversal chosen so
-// that both read patterns of the kernels spread over all banks: 16
-// consecutive rows read at the same chunk (ds_read_b128 of MFMA operands)
-// land on 16 distinct 4-bank groups, and the 4 rows x 64 bytes that a half
-// wave reads with ds_read_b64_tr_b16 land on disjoint chunk sets. At D=64
-// two rows share a 256-byte bank line, so f uses row / 2.
-template <int D>
-__device__ __forceinline__ int swz(int row, int col) {
-  int f;
-  if constexpr (D == 64) {
-    const int m = (row >> 1) & 7;
-    f = ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
-  } else {
-    static_assert(D == 128, "swizzle defined for D = 64, 128");
-    const int m = row & 15;
-    f = ((m & 1) << 3) | ((m & 2) << 1) | ((m >> 1) & 2) | ((m >> 3) & 1);
-  }
-  return row * D + ((((col >> 3) ^ f)) << 3) + (col & 7);
-}
-
 // 2^x on the transcendental unit (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -93,7 +93,10 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Under a causal mask the wave index is made visibly wave-uniform, so the
+  // per-wave mask decisions compile to scalar branches (measured faster
+  // there; the dense launch schedules better without it).
+  const int wave = CS == 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
