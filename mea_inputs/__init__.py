@@ -138,3 +138,24 @@ def decode_cache_rows(seed: int, b: int, n: int, Hkv: int, D: int, dtype: str):
     :func:`decode_case`. Lets a caller fill a large device cache row by row."""
     return (normal_bits(seed, (n, Hkv, D), dtype, _KC, b),
             normal_bits(seed, (n, Hkv, D), dtype, _VC, b))
+
+
+def random_block_mask(seed: int, n_qblocks: int, n_kblocks: int, density: float, keep_diagonal: bool = True):
+    """Seeded boolean block mask ``[n_qblocks, n_kblocks]`` (uint8 0/1): each
+    block on with probability ``density``; ``keep_diagonal`` also turns on
+    block (r, r) so no query block of a square case is left without keys."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7, 7])))
+    m = (rng.random((n_qblocks, n_kblocks)) < density)
+    if keep_diagonal:
+        r = np.arange(min(n_qblocks, n_kblocks))
+        m[r, r] = True
+    return m.astype(np.uint8)
+
+
+def band_global_block_mask(n_qblocks: int, n_kblocks: int, half_width: int, n_global: int):
+    """Sliding-window block pattern: query block r sees key blocks
+    r - half_width .. r + half_width, plus the first ``n_global`` key blocks
+    (global tokens), as uint8 ``[n_qblocks, n_kblocks]``."""
+    r = np.arange(n_qblocks)[:, None]
+    c = np.arange(n_kblocks)[None, :]
+    return ((np.abs(r - c) <= half_width) | (c < n_global)).astype(np.uint8)

@@ -12,6 +12,7 @@ form of ALiBi without a causal mask (it is tested against the stated reading
 only).
 """
 from .attention import (  # noqa: F401
+    BLOCK,
     attend,
     attend_grad,
     bwd,

@@ -44,6 +44,12 @@ Readings taken where the pages are silent (each also listed in the design doc):
 * decode: the newest token's k/v is already in the cache (briefia.fr page,
   section "Pre-remplissage et decodage"); its query, at position ctx-1,
   attends to cache rows 0..ctx-1;
+* block-sparse attention (the FlashAttention page, section on what the
+  numbers showed, names a block-sparse variant without defining it): a
+  boolean mask over blocks of ``BLOCK`` x ``BLOCK`` (query row, key) index
+  pairs, the same for every batch row and head; a pair is allowed only if its
+  block is on, and under a causal mask only if the causal rule allows it too.
+  Positions are the dense row and key indices (block (i // BLOCK, j // BLOCK));
 * backward: the gradients of the loss sum(dO * o) with respect to q, k and v
   (not the slopes, not the scale), for an upstream gradient dO. The
   FlashAttention page (section on the softmax that needs not see the whole
@@ -57,6 +63,8 @@ Readings taken where the pages are silent (each also listed in the design doc):
 from __future__ import annotations
 
 import numpy as np
+
+BLOCK = 64   # block edge of block-sparse masks (query rows and keys)
 
 
 def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
@@ -76,12 +84,13 @@ def kv_head(h: int, Hq: int, Hkv: int) -> int:
 
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
-           slopes=None, rows=None):
+           slopes=None, rows=None, block_mask=None):
     """Attention of one segment, float64 throughout.
 
     q ``[M, Hq, D]``, k and v ``[N, Hkv, D]`` (float64). ``rows`` optionally
-    selects which query rows to compute (default all). Returns
-    ``(o [len(rows), Hq, D], lse [Hq, len(rows)])``.
+    selects which query rows to compute (default all). ``block_mask``
+    (``[ceil(M/BLOCK), ceil(N/BLOCK)]`` booleans) keeps only the pairs whose
+    block is on. Returns ``(o [len(rows), Hq, D], lse [Hq, len(rows)])``.
     """
     M, Hq, D = q.shape
     N, Hkv, Dk = k.shape
@@ -95,6 +104,8 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bo
         allowed = j[None, :] <= pos_i[:, None]
     else:
         allowed = np.ones((len(i), N), dtype=bool)
+    if block_mask is not None:
+        allowed = allowed & np.asarray(block_mask, dtype=bool)[i[:, None] // BLOCK, j[None, :] // BLOCK]
     any_allowed = allowed.any(axis=1)
 
     o = np.zeros((len(i), Hq, D), dtype=np.float64)
@@ -126,7 +137,7 @@ def _segments(B, M, N, seqstart_q, seqstart_k):
 
 
 def fwd(q_bits, k_bits, v_bits, dtype: str, scale: float, causal: bool = False,
-        seqstart_q=None, seqstart_k=None, alibi_slopes=None):
+        seqstart_q=None, seqstart_k=None, alibi_slopes=None, block_mask=None):
     """Forward attention over bit-pattern inputs.
 
     Dense: q ``[B,M,Hq,D]``, k/v ``[B,N,Hkv,D]``. Packed (block-diagonal): q
@@ -135,9 +146,13 @@ def fwd(q_bits, k_bits, v_bits, dtype: str, scale: float, causal: bool = False,
     (tutorial section "Utilizzare Sequenze di Lunghezza Variabile",
     BlockDiagonalMask / BlockDiagonalCausalMask).
 
+    ``block_mask`` (dense only): see :func:`attend`.
+
     Returns ``(o, lse)``: o float64 shaped like q, lse ``[B, Hq, M]`` (dense)
     or ``[1, Hq, T_q]`` (packed).
     """
+    if block_mask is not None and seqstart_q is not None:
+        raise ValueError("block-sparse masks are defined for dense batches")
     q = decode_bits(q_bits, dtype)
     k = decode_bits(k_bits, dtype)
     v = decode_bits(v_bits, dtype)
@@ -146,14 +161,14 @@ def fwd(q_bits, k_bits, v_bits, dtype: str, scale: float, causal: bool = False,
     o = np.zeros_like(q)
     lse = np.full((B, Hq, M), -np.inf)
     for b, q0, q1, k0, k1 in _segments(B, M, N, seqstart_q, seqstart_k):
-        ob, lb = attend(q[b, q0:q1], k[b, k0:k1], v[b, k0:k1], scale, causal, alibi_slopes)
+        ob, lb = attend(q[b, q0:q1], k[b, k0:k1], v[b, k0:k1], scale, causal, alibi_slopes, block_mask=block_mask)
         o[b, q0:q1] = ob
         lse[b, :, q0:q1] = lb
     return o, lse
 
 
 def fwd_rows(q_bits, k_bits, v_bits, dtype: str, scale: float, b: int, rows, causal: bool = False,
-             seqstart_q=None, seqstart_k=None, segment: int | None = None, alibi_slopes=None):
+             seqstart_q=None, seqstart_k=None, segment: int | None = None, alibi_slopes=None, block_mask=None):
     """Selected query rows of :func:`fwd` for one batch row ``b`` (dense) or one
     packed ``segment`` (then ``rows`` are segment-local). Only that batch row
     or segment is decoded, so this stays cheap at full workload sizes."""
@@ -167,7 +182,7 @@ def fwd_rows(q_bits, k_bits, v_bits, dtype: str, scale: float, b: int, rows, cau
         q = decode_bits(q_bits[0, sq[segment]:sq[segment + 1]], dtype)
         k = decode_bits(k_bits[0, sk[segment]:sk[segment + 1]], dtype)
         v = decode_bits(v_bits[0, sk[segment]:sk[segment + 1]], dtype)
-    return attend(q, k, v, scale, causal, alibi_slopes, rows=rows)
+    return attend(q, k, v, scale, causal, alibi_slopes, rows=rows, block_mask=block_mask)
 
 
 def decode(q_bits, kcache_bits, vcache_bits, ctx_lens, dtype: str, scale: float,
@@ -231,7 +246,7 @@ def kv_append(kcache_bits, vcache_bits, k_new_bits, v_new_bits, ctx_lens):
 
 
 def attend_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                causal: bool = False, slopes=None):
+                causal: bool = False, slopes=None, block_mask=None):
     """Gradients of sum(do * attend(q, k, v)[0]) for one segment, float64.
 
     q, do ``[M, Hq, D]``; k, v ``[N, Hkv, D]``. The attention weights are
@@ -252,6 +267,8 @@ def attend_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, sca
     j = np.arange(N)
     pos = i + (N - M)
     allowed = (j[None, :] <= pos[:, None]) if causal else np.ones((M, N), dtype=bool)
+    if block_mask is not None:
+        allowed = allowed & np.asarray(block_mask, dtype=bool)[i[:, None] // BLOCK, j[None, :] // BLOCK]
     for h in range(Hq):
         g = kv_head(h, Hq, Hkv)
         s = sc * (q[:, h, :] @ k[:, g, :].T)
@@ -272,10 +289,12 @@ def attend_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, sca
 
 
 def bwd(q_bits, k_bits, v_bits, do_bits, dtype: str, scale: float, causal: bool = False,
-        seqstart_q=None, seqstart_k=None, alibi_slopes=None, batches=None):
+        seqstart_q=None, seqstart_k=None, alibi_slopes=None, batches=None, block_mask=None):
     """Backward of :func:`fwd` over bit-pattern inputs (same layouts; ``do``
     shaped like q). Returns float64 ``(dq, dk, dv)`` shaped like q, k, v.
     Dense batch rows not in ``batches`` are left NaN (packed inputs are one row)."""
+    if block_mask is not None and seqstart_q is not None:
+        raise ValueError("block-sparse masks are defined for dense batches")
     q = decode_bits(q_bits, dtype)
     k = decode_bits(k_bits, dtype)
     v = decode_bits(v_bits, dtype)
@@ -293,7 +312,8 @@ def bwd(q_bits, k_bits, v_bits, do_bits, dtype: str, scale: float, causal: bool 
     for b, q0, q1, k0, k1 in _segments(B, M, N, seqstart_q, seqstart_k):
         if b not in keep:
             continue
-        g = attend_grad(q[b, q0:q1], k[b, k0:k1], v[b, k0:k1], do[b, q0:q1], scale, causal, alibi_slopes)
+        g = attend_grad(q[b, q0:q1], k[b, k0:k1], v[b, k0:k1], do[b, q0:q1], scale, causal, alibi_slopes,
+                        block_mask=block_mask)
         dq[b, q0:q1] = g[0]
         dk[b, k0:k1] = g[1]
         dv[b, k0:k1] = g[2]

@@ -465,6 +465,64 @@ def check_bwd_blockdiag_and_gqa(orc):
             summed = rr.reshape(2, 9, 2, 3, 8).sum(axis=3)
             assert _maxerr(a, summed) < TOL, ("bwd gqa dk/dv", causal)
 
+
+# --- block-sparse ----------------------------------------------------------------
+
+def _expand_blocks(bm, M, N, B=64):
+    """Block mask -> per-element boolean mask [M, N] (np.kron, independent of the oracle's indexing)."""
+    full = np.kron(np.asarray(bm, dtype=bool), np.ones((B, B), dtype=bool))
+    return full[:M, :N]
+
+
+def check_blocksparse_sdpa_bool_mask(orc):
+    """Block-sparse attention == torch SDPA with the element-level boolean
+    mask the blocks expand to (np.kron), alone and ANDed with the causal
+    rule; forward and backward (torch autograd)."""
+    for seed, (B, M, N, Hq, Hkv, D), causal in [(41, (2, 150, 200, 4, 2, 8), False), (42, (1, 190, 190, 2, 2, 8), True)]:
+        c = inp.dense_case(seed, B, M, N, Hq, Hkv, D, "bf16")
+        nq, nk = -(-M // 64), -(-N // 64)
+        bm = inp.random_block_mask(seed, nq, nk, 0.5)
+        el = _expand_blocks(bm, M, N)
+        if causal:
+            el = el & np.tril(np.ones((M, N), dtype=bool), N - M)
+        assert el.any(axis=1).all()
+        mask = torch.from_numpy(el)[None, None]
+        scale = 0.3
+        o, lse = orc.fwd(c["q"], c["k"], c["v"], "bf16", scale, causal=causal, block_mask=bm)
+        tq, tk, tv = (_torch_decode(c[x], "bf16") for x in ("q", "k", "v"))
+        ref = _sdpa(tq, tk, tv, float(np.float32(scale)), mask=mask, gqa=Hq != Hkv)
+        assert _maxerr(o, ref) < TOL, ("blocksparse fwd", seed, _maxerr(o, ref))
+        do = inp.normal_bits(seed + 100, (B, M, Hq, D), "bf16", 0)
+        g = orc.bwd(c["q"], c["k"], c["v"], do, "bf16", scale, causal=causal, block_mask=bm)
+        gr = _autograd_sdpa(tq, tk, tv, _torch_decode(do, "bf16"), float(np.float32(scale)), mask=mask,
+                            gqa=Hq != Hkv)
+        for name, a, r in zip("qkv", g, gr):
+            assert _maxerr(a, r) < TOL, ("blocksparse bwd", seed, name, _maxerr(a, r))
+
+
+def check_blocksparse_all_on_is_dense(orc):
+    c = inp.dense_case(43, 1, 130, 70, 2, 1, 8, "fp16")
+    ones = np.ones((3, 2), np.uint8)
+    for causal in (False, True):
+        a = orc.fwd(c["q"], c["k"], c["v"], "fp16", 0.4, causal=causal)
+        b = orc.fwd(c["q"], c["k"], c["v"], "fp16", 0.4, causal=causal, block_mask=ones)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), ("all-on mask", causal)
+
+
+def check_blocksparse_masked_blocks_do_not_matter(orc):
+    """Rows never read K/V of blocks that are off for them; a query block with
+    every block off returns 0 and lse -inf."""
+    c = inp.dense_case(44, 1, 192, 256, 2, 2, 8, "bf16")
+    bm = np.array([[1, 0, 1, 0], [0, 0, 0, 0], [1, 1, 0, 1]], np.uint8)
+    o, lse = orc.fwd(c["q"], c["k"], c["v"], "bf16", 0.5, block_mask=bm)
+    k2, v2 = c["k"].copy(), c["v"].copy()
+    k2[:, 64:128] = inp.normal_bits(45, k2[:, 64:128].shape, "bf16", 0)    # key block 1: off for query block 0
+    v2[:, 192:256] = inp.normal_bits(45, v2[:, 192:256].shape, "bf16", 1)  # key block 3: off for query block 0
+    o2, _ = orc.fwd(c["q"], k2, v2, "bf16", 0.5, block_mask=bm)
+    assert np.array_equal(o[:, :64], o2[:, :64]), "masked blocks leak"
+    assert not np.array_equal(o[:, 128:], o2[:, 128:]), "query block 2 must see key blocks 1 and 3"
+    assert np.all(o[:, 64:128] == 0) and np.all(np.isneginf(lse[:, :, 64:128])), "empty query block"
+
 ALL_CHECKS = [
     check_sdpa_nomask,
     check_sdpa_causal_square,
@@ -492,4 +550,7 @@ ALL_CHECKS = [
     check_bwd_zero_query_closed_form,
     check_bwd_constant_v,
     check_bwd_blockdiag_and_gqa,
+    check_blocksparse_sdpa_bool_mask,
+    check_blocksparse_all_on_is_dense,
+    check_blocksparse_masked_blocks_do_not_matter,
 ]

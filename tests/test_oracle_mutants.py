@@ -52,6 +52,13 @@ MUTANTS = {
     "bwd_top_left": ("pos = i + (N - M)", "pos = i"),
     "bwd_alibi_sign": ("s = s - float(np.float32(slopes[h])) * np.abs", "s = s + float(np.float32(slopes[h])) * np.abs"),
     "bwd_unnormalised_p": ("p = e / np.where(tot > 0, tot, 1.0)", "p = e"),
+    "blocksparse_transposed": ("allowed = allowed & np.asarray(block_mask, dtype=bool)[i[:, None] // BLOCK, j[None, :] // BLOCK]\n    any_allowed",
+                               "allowed = allowed & np.asarray(block_mask, dtype=bool).T[j[None, :] // BLOCK, i[:, None] // BLOCK].T\n    any_allowed"),
+    "blocksparse_block_32": ("BLOCK = 64", "BLOCK = 32"),
+    "blocksparse_ignored_fwd": ("allowed = allowed & np.asarray(block_mask, dtype=bool)[i[:, None] // BLOCK, j[None, :] // BLOCK]\n    any_allowed",
+                                "pass\n    any_allowed"),
+    "blocksparse_ignored_bwd": ("allowed = allowed & np.asarray(block_mask, dtype=bool)[i[:, None] // BLOCK, j[None, :] // BLOCK]\n    for h",
+                                "pass\n    for h"),
 }
 
 
