@@ -89,6 +89,32 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out,
             const float* alibi_slopes, int dtype, float* lse, void* stream);
 
 /*
+ * mea_fwd_blocksparse - mea_fwd restricted to a block-sparse pattern: the
+ * (query row, key) index space of every batch row and head is cut into
+ * blocks of mea_block_sparse_block() x mea_block_sparse_block() (64 x 64),
+ * and a pair is allowed only if its block is on (and, with MEA_MASK_CAUSAL,
+ * the causal rule allows it). Blocks that are off are never loaded or
+ * computed: each work-group walks a skip list of the key blocks its query
+ * blocks need. The FlashAttention page names this block-sparse variant as
+ * what reached 64K-element sequences ("FlashAttention (2022): l'attenzione
+ * che non satura la memoria", paithon.it, section on what the numbers
+ * showed); the pages give no pattern, so the mask is the caller's.
+ *
+ *   q, out [B, M, Hq, D]; k, v [B, N, Hkv, D] (dense layout of mea_fwd)
+ *   block_mask  uint8 device array [ceil(M/64)][ceil(N/64)], row-major, shared
+ *               by all batch rows and heads; nonzero = block on. Required.
+ * bias_kind  MEA_MASK_CAUSAL and/or MEA_BIAS_ALIBI (MEA_MASK_BLOCKDIAG is
+ *            MEA_EINVAL). Rows whose blocks are all off get out = 0, lse = -inf.
+ * Other arguments, lse layout and errors as mea_fwd.
+ */
+int mea_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv,
+                        int D, float scale, unsigned bias_kind, const uint8_t* block_mask, const float* alibi_slopes,
+                        int dtype, float* lse, void* stream);
+
+/* Block edge (query rows and keys) of mea_fwd_blocksparse masks: 64. */
+int mea_block_sparse_block(void);
+
+/*
  * mea_bwd - backward pass of mea_fwd: the gradients dq, dk, dv of the loss
  * sum(dout * out) for the same (q, k, v, masks, bias). The scores are
  * recomputed block by block from q, k and the forward's lse, never stored

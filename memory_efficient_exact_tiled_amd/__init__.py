@@ -5,6 +5,7 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 
 * :func:`fwd` - tiled exact attention forward (causal, packed block-diagonal,
   grouped-query, ALiBi);
+* :func:`fwd_blocksparse` - the forward over a 64 x 64 block-sparse pattern;
 * :func:`bwd` - its backward (dq, dk, dv with the scores recomputed);
 * :func:`decode` - one KV-cache decode step (split-KV partials + combine);
 * :func:`fwd_kvcache` - chunked prefill / multi-token decode over a KV cache;
@@ -28,11 +29,13 @@ from ._binding import (  # noqa: F401
     MEA_OK,
     MeaError,
     bwd,
+    block_sparse_block,
     bwd_workspace_bytes,
     decode,
     decode_chunk,
     decode_workspace_bytes,
     fwd,
+    fwd_blocksparse,
     fwd_kvcache,
     kv_append,
     lib,

@@ -23,7 +23,7 @@ MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP = 0, 1, 2, 3, 4
 MEA_FP16, MEA_BF16 = 0, 1
 MEA_MASK_CAUSAL, MEA_MASK_BLOCKDIAG, MEA_BIAS_ALIBI = 1, 2, 4
 
-EXPORTS = ("mea_fwd", "mea_bwd", "mea_bwd_workspace_bytes", "mea_fwd_kvcache", "mea_kv_append", "mea_decode",
+EXPORTS = ("mea_fwd", "mea_fwd_blocksparse", "mea_block_sparse_block", "mea_bwd", "mea_bwd_workspace_bytes", "mea_fwd_kvcache", "mea_kv_append", "mea_decode",
            "mea_decode_workspace_bytes", "mea_strerror", "mea_supported", "mea_decode_chunk")
 
 if not os.path.exists(LIB_PATH):
@@ -33,6 +33,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i, _f, _u, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
 _lib.mea_fwd.restype = _i
 _lib.mea_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp, _i, _vp, _vp]
+_lib.mea_fwd_blocksparse.restype = _i
+_lib.mea_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _i, _vp, _vp]
+_lib.mea_block_sparse_block.restype = _i
+_lib.mea_block_sparse_block.argtypes = []
 _lib.mea_bwd.restype = _i
 _lib.mea_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp,
                          _i, _vp, _sz, _vp]
@@ -159,6 +163,35 @@ def fwd(q, k, v, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alib
     _check(_lib.mea_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, M, N, Hq, Hkv, D, float(scale), kind,
                         _ptr(seqstart_q), _ptr(seqstart_k), _ptr(alibi_slopes), _dtype_code(q), _ptr(lse),
                         _stream(stream)))
+    return out
+
+
+def block_sparse_block() -> int:
+    return int(_lib.mea_block_sparse_block())
+
+
+def fwd_blocksparse(q, k, v, block_mask, *, causal: bool = False, alibi_slopes=None, scale: float | None = None,
+                    out=None, lse=None, stream=None):
+    """Block-sparse exact attention forward (``mea_fwd_blocksparse``): dense
+    q ``[B,M,Hq,D]``, k/v ``[B,N,Hkv,D]``; ``block_mask`` uint8 (or bool)
+    device tensor ``[ceil(M/64), ceil(N/64)]``, nonzero = block on."""
+    torch = _torch()
+    B, M, N, Hq, Hkv, D = _shapes(q, k, None, None)
+    if v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match in shape and dtype, and q, k, v in dtype")
+    blk = block_sparse_block()
+    if block_mask.dtype not in (torch.uint8, torch.bool) or tuple(block_mask.shape) != (-(-M // blk), -(-N // blk)):
+        raise ValueError(f"block_mask must be uint8/bool [{-(-M // blk)}, {-(-N // blk)}]")
+    if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
+        raise TypeError("alibi_slopes must be float32")
+    _need_cuda(q, k, v, out, lse, alibi_slopes, block_mask)
+    out = torch.empty_like(q) if out is None else out
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kind = (MEA_MASK_CAUSAL if causal else 0) | (MEA_BIAS_ALIBI if alibi_slopes is not None else 0)
+    _check(_lib.mea_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, M, N, Hq, Hkv, D, float(scale), kind,
+                                    _ptr(block_mask), _ptr(alibi_slopes), _dtype_code(q), _ptr(lse),
+                                    _stream(stream)))
     return out
 
 

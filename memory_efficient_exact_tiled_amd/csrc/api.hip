@@ -79,7 +79,8 @@ namespace {
 // Shared by mea_fwd and mea_fwd_kvcache: validates, fills FwdParams, launches.
 int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv, int D,
              float scale, unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
-             const float* alibi_slopes, int dtype, float* lse, const int32_t* kv_lens, void* stream) {
+             const float* alibi_slopes, int dtype, float* lse, const int32_t* kv_lens, const uint8_t* block_mask,
+             void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return MEA_EINVAL;
   if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return MEA_EINVAL;
   if (Hq % Hkv != 0) return MEA_EINVAL;
@@ -98,7 +99,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
   // offsets are 64-bit.
   const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
   if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
-  const int BM = mea::fwd_block_m(D, causal);
+  if (block_mask != nullptr && (varlen || kv_lens != nullptr)) return MEA_EINVAL;
+  const int BM = mea::fwd_block_m(D, causal, block_mask != nullptr);
 
   mea::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -110,6 +112,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
   p.seqstart_k = seqstart_k != nullptr ? seqstart_k : seqstart_q;
   p.slopes = alibi_slopes;
   p.kv_lens = kv_lens;
+  p.block_mask = block_mask;
+  p.nkb = (N + mea::kSparseBlock - 1) / mea::kSparseBlock;
   p.B = B;
   p.M = M;
   p.N = N;
@@ -160,8 +164,19 @@ int mea_fwd(const void* q, const void* k, const void* v, void* out, int B, int M
             float scale, unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k,
             const float* alibi_slopes, int dtype, float* lse, void* stream) {
   return fwd_impl(q, k, v, out, B, M, N, Hq, Hkv, D, scale, bias_kind, seqstart_q, seqstart_k, alibi_slopes, dtype,
-                  lse, nullptr, stream);
+                  lse, nullptr, nullptr, stream);
 }
+
+int mea_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, int B, int M, int N, int Hq, int Hkv,
+                        int D, float scale, unsigned bias_kind, const uint8_t* block_mask, const float* alibi_slopes,
+                        int dtype, float* lse, void* stream) {
+  if (block_mask == nullptr) return MEA_EINVAL;
+  if ((bias_kind & MEA_MASK_BLOCKDIAG) != 0u) return MEA_EINVAL;
+  return fwd_impl(q, k, v, out, B, M, N, Hq, Hkv, D, scale, bias_kind, nullptr, nullptr, alibi_slopes, dtype, lse,
+                  nullptr, block_mask, stream);
+}
+
+int mea_block_sparse_block(void) { return mea::kSparseBlock; }
 
 int mea_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out,
                     int B, int M, int Hq, int Hkv, int D, int S_max, float scale, unsigned bias_kind,
@@ -169,7 +184,7 @@ int mea_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const
   if (ctx_lens == nullptr) return MEA_EINVAL;
   if ((bias_kind & MEA_MASK_BLOCKDIAG) != 0u) return MEA_EINVAL;
   return fwd_impl(q, kcache, vcache, out, B, M, S_max, Hq, Hkv, D, scale, bias_kind, nullptr, nullptr, alibi_slopes,
-                  dtype, lse, ctx_lens, stream);
+                  dtype, lse, ctx_lens, nullptr, stream);
 }
 
 int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new, const int32_t* ctx_lens, int B,

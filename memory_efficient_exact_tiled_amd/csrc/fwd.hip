@@ -34,7 +34,11 @@
 //     above the diagonal are never visited (per work-group) or computed (per
 //     wave); ALiBi is computed from the indices;
 //   * grouped-query attention: query head h reads KV head h / (Hq / Hkv) in
-//     place; the heads sharing a KV head are adjacent in the launch order.
+//     place; the heads sharing a KV head are adjacent in the launch order;
+//   * block-sparse masks (64 x 64 blocks of query rows and keys): the
+//     work-group walks only the key blocks at least one of its query blocks
+//     has on (a skip list read from the mask), and a wave skips the blocks
+//     that are off for its own query block.
 //
 // Launch order: work-group p runs on XCD p % 8; each XCD is given a
 // contiguous range of logical work-groups, so the query tiles of one head
@@ -75,8 +79,9 @@ struct FwdShape {
 // CS and AL select how the causal and ALiBi flags are known: 0 = off, 1 = on
 // (compile-time constants), 2 = read from p at run time. Causal launches
 // specialise both; the dense launch reads both at run time, which the
-// compiler schedules better than the fully specialised form.
-template <typename T, int D, int QB_, int CS, int AL>
+// compiler schedules better than the fully specialised form. BS = 1 reads a
+// block-sparse mask (p.block_mask).
+template <typename T, int D, int QB_, int CS, int AL, int BS = 0>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE))) fwd_kernel(const FwdParams p) {
   using S = FwdShape<D, QB_>;
@@ -225,16 +230,39 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   // blocks go in order, so the work-groups of a head read the same K/V
   // blocks at about the same time (L2 reuse).
   const bool rev = CS == 1 && AL == 1;
-  if (ntiles > 0) gload(rev ? ntiles - 1 : 0);
-  for (int it = 0; it < ntiles; ++it) {
+  // Block-sparse skip list: key block kt is visited if any query block of the
+  // work-group has it on (the mask row of query block r is p.block_mask + r *
+  // p.nkb; K tiles are exactly the mask's key blocks).
+  int qblo = 0, qbhi = -1, wqblk = -1;
+  if (BS) {
+    qblo = i0 >> 6;
+    qbhi = min(i0 + BM, M_s) - 1;
+    qbhi = qbhi >= i0 ? (qbhi >> 6) : qblo - 1;
+    wqblk = (wq0 < M_s) ? (wq0 >> 6) : -1;
+  }
+  auto next_tile = [&](int it) {
+    if (BS) {
+      for (; it < ntiles; ++it) {
+        bool on = false;
+        for (int r = qblo; r <= qbhi; ++r) on |= p.block_mask[(long long)r * p.nkb + it] != 0;
+        if (on) break;
+      }
+    }
+    return it;
+  };
+  int it0 = next_tile(0), nit = 0;
+  if (it0 < ntiles) gload(rev ? ntiles - 1 - it0 : it0);
+  for (int it = it0, n = 0; it < ntiles; it = nit, ++n) {
     const int kt = rev ? ntiles - 1 - it : it;
-    const int buf = it & 1;
+    const int buf = BS ? (n & 1) : (it & 1);
+    nit = next_tile(it + 1);
     lstore(buf);
     __syncthreads();
-    if (it + 1 < ntiles) gload(rev ? kt - 1 : kt + 1);
+    if (nit < ntiles) gload(rev ? ntiles - 1 - nit : nit);
 
     const int key_base = kt * kBN;
     if (key_base >= wkend) continue;   // the whole block is masked for this wave
+    if (BS && (wqblk < 0 || p.block_mask[(long long)wqblk * p.nkb + kt] == 0)) continue;
     const uint16_t* Ks = smem + buf * 2 * TILE;
     const uint16_t* Vs = Ks + TILE;
 
@@ -378,7 +406,9 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
 template <typename T, int D, int QB, bool CAUSAL>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
   const int grid = p.wg_per_xcd * 8;
-  if (!CAUSAL)
+  if (p.block_mask != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 2, 2, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  else if (!CAUSAL)
     hipLaunchKernelGGL((fwd_kernel<T, D, QB, 2, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   else if (p.alibi)
     hipLaunchKernelGGL((fwd_kernel<T, D, QB, 1, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
@@ -389,14 +419,16 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
-  if (D == 64) return p.causal ? launch_typed<T, 64, 1, true>(p, stream) : launch_typed<T, 64, 2, false>(p, stream);
+  if (D == 64)
+    return (p.causal && p.block_mask == nullptr) ? launch_typed<T, 64, 1, true>(p, stream)
+                                                 : launch_typed<T, 64, 2, false>(p, stream);
   return p.causal ? launch_typed<T, 128, 1, true>(p, stream) : launch_typed<T, 128, 1, false>(p, stream);
 }
 
 }  // namespace
 
-int fwd_block_m(int D, bool causal) {
-  if (D == 64) return causal ? FwdShape<64, 1>::BM : FwdShape<64, 2>::BM;
+int fwd_block_m(int D, bool causal, bool block_sparse) {
+  if (D == 64) return (causal && !block_sparse) ? FwdShape<64, 1>::BM : FwdShape<64, 2>::BM;
   return FwdShape<128, 1>::BM;
 }
 

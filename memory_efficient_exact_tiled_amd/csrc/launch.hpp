@@ -16,6 +16,8 @@ struct FwdParams {
   const int32_t* seqstart_k;
   const float* slopes;
   const int32_t* kv_lens;  // dense mode only, nullable: per-batch key count (clamped to N)
+  const uint8_t* block_mask;  // dense mode only, nullable: [ceil(M/64)][nkb] block-sparse mask
+  int nkb;                 // key blocks per mask row: ceil(N/64)
   int B, M, N, Hq, Hkv, group;
   int causal, varlen, alibi;
   float scale_log2;      // scale * log2(e)
@@ -71,7 +73,8 @@ struct BwdParams {
 };
 
 // Query rows per forward work-group and the decode chunk length.
-int fwd_block_m(int D, bool causal);
+int fwd_block_m(int D, bool causal, bool block_sparse);
+constexpr int kSparseBlock = 64;   // block edge of block-sparse masks
 constexpr int kDecodeChunk = 512;
 
 struct AppendParams {

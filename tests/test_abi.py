@@ -141,6 +141,20 @@ def test_bwd_workspace_bytes():
     assert mea.bwd_workspace_bytes(0, 64, 4, 0) == 0
 
 
+def test_blocksparse_rejects():
+    lib = mea.lib()
+    args = [FAKE, FAKE, FAKE, FAKE, 2, 128, 128, 4, 2, 64, 0.125, 0, FAKE, None, mea.MEA_BF16, None, None]
+    assert mea.block_sparse_block() == 64
+    a = list(args); a[12] = None                       # no mask
+    assert lib.mea_fwd_blocksparse(*a) == mea.MEA_EINVAL
+    a = list(args); a[11] = mea.MEA_MASK_BLOCKDIAG     # packed batches have no block-sparse form
+    assert lib.mea_fwd_blocksparse(*a) == mea.MEA_EINVAL
+    a = list(args); a[11] = mea.MEA_BIAS_ALIBI         # ALiBi without slopes
+    assert lib.mea_fwd_blocksparse(*a) == mea.MEA_EINVAL
+    a = list(args); a[9] = 80
+    assert lib.mea_fwd_blocksparse(*a) == mea.MEA_EUNSUPPORTED
+
+
 def test_product_package_does_not_reach_the_oracle():
     """The product package neither imports nor names the oracle."""
     pkg = os.path.join(ROOT, "memory_efficient_exact_tiled_amd")

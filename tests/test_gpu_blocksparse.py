@@ -1,0 +1,96 @@
+"""Parity of the block-sparse forward (``mea_fwd_blocksparse``) with the fp64 oracle, on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import mea_inputs as inp
+import oracle.attention as orc
+from gpu_util import LSE_TOL, TOL, dev, f32, host_f64, report, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_efficient_exact_tiled_amd as m
+    return m
+
+
+def _mask(bm):
+    return torch.from_numpy(np.ascontiguousarray(bm, dtype=np.uint8)).cuda()
+
+
+def _run(mea, c, dt, bm, causal=False, slopes=None):
+    q, k, v = dev(c["q"], dt), dev(c["k"], dt), dev(c["v"], dt)
+    B, M, Hq, D = c["q"].shape
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    lse = torch.full((B, Hq, M), 7.0, dtype=torch.float32, device="cuda")
+    out = mea.fwd_blocksparse(q, k, v, _mask(bm), causal=causal, scale=scale,
+                              alibi_slopes=None if slopes is None else f32(slopes), lse=lse)
+    torch.cuda.synchronize()
+    return out, lse, scale
+
+
+CASES = [
+    # name, seed, B, M, N, Hq, Hkv, D, dtype, causal, alibi, density
+    ("ragged_m300_n260_d64_bf16_gqa", 0, 2, 300, 260, 4, 2, 64, "bf16", False, False, 0.4),
+    ("causal_alibi_m333_d128_fp16", 1, 1, 333, 333, 4, 4, 128, "fp16", True, True, 0.5),
+    ("causal_m512_d64_bf16_sparse", 2, 2, 512, 512, 8, 2, 64, "bf16", True, False, 0.25),
+    ("noncausal_alibi_m200_n700_d128_bf16", 3, 1, 200, 700, 2, 1, 128, "bf16", False, True, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_blocksparse_parity(mea, case):
+    name, seed, B, M, N, Hq, Hkv, D, dt, causal, alibi, dens = case
+    say(f"case blocksparse {name}")
+    c = inp.dense_case(seed, B, M, N, Hq, Hkv, D, dt)
+    bm = inp.random_block_mask(seed, -(-M // 64), -(-N // 64), dens)
+    bm[-1, :] = 0                      # one query block with no key at all
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    out, lse, scale = _run(mea, c, dt, bm, causal=causal, slopes=slopes)
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=causal, alibi_slopes=slopes, block_mask=bm)
+    err = report(name, host_f64(out), want, TOL[dt])
+    assert err <= TOL[dt]
+    got_lse = lse.cpu().numpy()
+    fin = np.isfinite(wlse)
+    assert np.array_equal(np.isfinite(got_lse), fin), "lse -inf pattern"
+    assert np.max(np.abs(got_lse[fin] - wlse[fin]), initial=0.0) <= LSE_TOL[dt], "lse"
+    assert np.all(host_f64(out)[:, (bm.shape[0] - 1) * 64:] == 0), "query block with every block off"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_all_on_mask_is_the_dense_kernel_bitwise(mea, D):
+    """With every block on, the skip list visits every key block in order:
+    the same arithmetic as the dense forward."""
+    say(f"case blocksparse all-on D={D}")
+    c = inp.dense_case(4 + D, 2, 257, 300, 4, 2, D, "bf16")
+    q, k, v = dev(c["q"], "bf16"), dev(c["k"], "bf16"), dev(c["v"], "bf16")
+    ones = torch.ones((-(-257 // 64), -(-300 // 64)), dtype=torch.uint8, device="cuda")
+    a = mea.fwd(q, k, v)
+    b = mea.fwd_blocksparse(q, k, v, ones)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_band_global_full_size_sampled(mea):
+    """B=1, M=N=16384, H=16, D=64, bf16 with a sliding window of 3 blocks on
+    each side plus one global key block, causal: sampled rows of two heads
+    against the oracle."""
+    say("case blocksparse band_global m16384")
+    B, M, H, D = 1, 16384, 16, 64
+    c = inp.dense_case(40, B, M, M, H, H, D, "bf16")
+    bm = inp.band_global_block_mask(M // 64, M // 64, 3, 1)
+    out, lse, scale = _run(mea, c, "bf16", bm, causal=True)
+    got = host_f64(out)
+    rng = np.random.default_rng(16384)
+    rows = np.unique(np.concatenate([[0, 63, 64, 200, 4095, 8191, M - 1], rng.integers(0, M, 25)]))
+    for h in (0, 11):
+        sl = (slice(0, 1), slice(None), slice(h, h + 1))
+        want, wlse = orc.fwd_rows(c["q"][sl], c["k"][sl], c["v"][sl], "bf16", scale, 0, rows, causal=True,
+                                  block_mask=bm)
+        err = report(f"band_global h{h}", got[0, rows, h:h + 1], want, TOL["bf16"])
+        assert err <= TOL["bf16"]
+        assert np.max(np.abs(lse[0, h, rows].cpu().numpy() - wlse[0])) <= LSE_TOL["bf16"]
