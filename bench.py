@@ -10,7 +10,10 @@ input already resident in HBM:
      Hkv=8, D=128, bf16, block-diagonal causal mask + ALiBi
   4. decode step, B=32, contexts uniform in [1024, 32768], Hq=32, Hkv=8,
      D=128, bf16 KV cache of 32768 slots per sequence
-  5. backward (dq, dk, dv) of items 1 and 2, from their stored output and
+  5. block-sparse forward, B=1, M=N=16384, H=16, D=64, bf16, causal, 64x64
+     blocks: a sliding window of 3 blocks on each side plus one global key
+     block (4*D flops per allowed query-key pair)
+  6. backward (dq, dk, dv) of items 1 and 2, from their stored output and
      lse and a seeded upstream gradient (10*D algorithmic flops per allowed
      query-key pair: S recomputed, dP, dV, dK, dQ)
 
@@ -232,7 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode,bwd_noncausal,bwd_causal",
+    ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode,fwd_blocksparse,"
+                                       "bwd_noncausal,bwd_causal",
                     help="comma-separated subset of the step to run (for profiling one kernel)")
     ap.add_argument("--table", action="store_true",
                     help="reproduce the tutorial's naive-vs-memory-efficient table (ms, peak MB) for seqlen 512..4096")
@@ -282,6 +286,16 @@ def main():
         fb[cz] = (o_, lse_, torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
                   torch.empty(mea.bwd_workspace_bytes(B_, M_, H_, int(cz)), dtype=torch.uint8, device="cuda"))
 
+    # Block-sparse item: its own inputs (16K tokens) and mask.
+    MS = 16384
+    bs_host = inp.dense_case(12, 1, MS, MS, 16, 16, 64, "bf16")
+    bs = {k_: to_dev(bs_host[k_], torch) for k_ in ("q", "k", "v")}
+    bmask_host = inp.band_global_block_mask(MS // 64, MS // 64, 3, 1)
+    bmask = torch.from_numpy(bmask_host).cuda()
+    out_bs = torch.empty_like(bs["q"])
+    r_, c_ = np.nonzero(bmask_host)
+    bs_pairs = float(np.sum(np.where(c_ < r_, 64 * 64, np.where(c_ == r_, 64 * 65 // 2, 0))))
+
     def bwd_item(cz):
         o_, lse_, gq, gk, gv, wsb = fb[cz]
         return lambda: mea.bwd(d["q"], d["k"], d["v"], o_, dout, lse_, causal=cz, dq=gq, dk=gk, dv=gv, workspace=wsb)
@@ -292,6 +306,7 @@ def main():
         ("fwd_varlen", lambda: mea.fwd(vl["q"], vl["k"], vl["v"], causal=True, seqstart_q=vl["seqstart"],
                                        alibi_slopes=vl["slopes"], out=out_v)),
         ("decode", lambda: mea.decode(dc["q"], dc["kc"], dc["vc"], dc["ctx"], out=out_dec, workspace=ws)),
+        ("fwd_blocksparse", lambda: mea.fwd_blocksparse(bs["q"], bs["k"], bs["v"], bmask, causal=True, out=out_bs)),
         ("bwd_noncausal", bwd_item(False)),
         ("bwd_causal", bwd_item(True)),
     ]
@@ -331,6 +346,7 @@ def main():
         "fwd_noncausal": 4.0 * 4 * 16 * 4096 * 4096 * 64,
         "fwd_causal": 4.0 * 4 * 16 * 64 * (4096 * 4097 / 2),
         "fwd_varlen": 4.0 * 128 * 32 * float(np.sum(L * (L + 1) // 2)),
+        "fwd_blocksparse": 4.0 * 64 * 16 * bs_pairs,
         "bwd_noncausal": 10.0 * 4 * 16 * 4096 * 4096 * 64,
         "bwd_causal": 10.0 * 4 * 16 * 64 * (4096 * 4097 / 2),
     }
@@ -369,6 +385,7 @@ def main():
             "workload": "attention forward B=4 M=N=4096 H=16 D=64 bf16 (no mask; causal beside it) "
                         "+ packed 8x[64,2048] Hq=32 Hkv=8 D=128 block-diag causal ALiBi "
                         "+ decode B=32 ctx[1024,32768] Hq=32 Hkv=8 D=128 "
+                        "+ block-sparse causal B=1 M=16384 H=16 D=64 (window 3 blocks + 1 global, 64x64) "
                         "+ backward of the two B=4 M=4096 forwards",
             "items": sorted(ms),
             "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)",

@@ -152,6 +152,18 @@ int mea_bwd(const void* q, const void* k, const void* v, const void* out, const 
             int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mea_bwd_blocksparse - mea_bwd for a mea_fwd_blocksparse call: the same
+ * arguments as that call (block_mask included) plus its out and lse, the
+ * upstream gradient, the gradient outputs and the workspace of mea_bwd.
+ * Blocks that are off are never loaded or computed; keys whose blocks are all
+ * off get dk = dv = 0.
+ */
+int mea_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D,
+                        float scale, unsigned bias_kind, const uint8_t* block_mask, const float* alibi_slopes,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mea_fwd_kvcache - chunked prefill / multi-token decode over a KV cache:
  * the M newest queries of every sequence attend to that sequence's cached
  * keys and values, whose rows for those M tokens are already appended. The

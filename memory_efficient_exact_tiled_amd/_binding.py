@@ -23,7 +23,7 @@ MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP = 0, 1, 2, 3, 4
 MEA_FP16, MEA_BF16 = 0, 1
 MEA_MASK_CAUSAL, MEA_MASK_BLOCKDIAG, MEA_BIAS_ALIBI = 1, 2, 4
 
-EXPORTS = ("mea_fwd", "mea_fwd_blocksparse", "mea_block_sparse_block", "mea_bwd", "mea_bwd_workspace_bytes", "mea_fwd_kvcache", "mea_kv_append", "mea_decode",
+EXPORTS = ("mea_fwd", "mea_fwd_blocksparse", "mea_block_sparse_block", "mea_bwd", "mea_bwd_blocksparse", "mea_bwd_workspace_bytes", "mea_fwd_kvcache", "mea_kv_append", "mea_decode",
            "mea_decode_workspace_bytes", "mea_strerror", "mea_supported", "mea_decode_chunk")
 
 if not os.path.exists(LIB_PATH):
@@ -40,6 +40,9 @@ _lib.mea_block_sparse_block.argtypes = []
 _lib.mea_bwd.restype = _i
 _lib.mea_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u, _vp, _vp, _vp,
                          _i, _vp, _sz, _vp]
+_lib.mea_bwd_blocksparse.restype = _i
+_lib.mea_bwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _u,
+                                     _vp, _vp, _i, _vp, _sz, _vp]
 _lib.mea_bwd_workspace_bytes.restype = _sz
 _lib.mea_bwd_workspace_bytes.argtypes = [_i, _i, _i, _u]
 _lib.mea_fwd_kvcache.restype = _i
@@ -214,10 +217,12 @@ def _shapes(q, k, seqstart_q, seqstart_k):
 
 
 def bwd(q, k, v, out, dout, lse, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alibi_slopes=None,
-        scale: float | None = None, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward of :func:`fwd` (``mea_bwd``): gradients of ``sum(dout * out)``.
+        scale: float | None = None, dq=None, dk=None, dv=None, workspace=None, block_mask=None, stream=None):
+    """Backward of :func:`fwd` (``mea_bwd``), or of :func:`fwd_blocksparse`
+    when ``block_mask`` is given (``mea_bwd_blocksparse``): gradients of
+    ``sum(dout * out)``.
 
-    ``out`` and ``lse`` are what :func:`fwd` returned/filled for the same
+    ``out`` and ``lse`` are what the forward returned/filled for the same
     arguments; ``dout`` is shaped like q. The workspace is allocated with torch
     when not given. Returns ``(dq, dk, dv)``.
     """
@@ -241,10 +246,20 @@ def bwd(q, k, v, out, dout, lse, *, causal: bool = False, seqstart_q=None, seqst
         workspace = torch.empty(bwd_workspace_bytes(B, M, Hq, kind), dtype=torch.uint8, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    nbytes = workspace.numel() * workspace.element_size()
+    if block_mask is not None:
+        blk = block_sparse_block()
+        if seqstart_q is not None or tuple(block_mask.shape) != (-(-M // blk), -(-N // blk)):
+            raise ValueError("block_mask needs dense inputs and shape [ceil(M/64), ceil(N/64)]")
+        _need_cuda(block_mask)
+        _check(_lib.mea_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), B, M, N, Hq, Hkv, D, float(scale), kind,
+                                        _ptr(block_mask), _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace),
+                                        nbytes, _stream(stream)))
+        return dq, dk, dv
     _check(_lib.mea_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         B, M, N, Hq, Hkv, D, float(scale), kind, _ptr(seqstart_q), _ptr(seqstart_k),
-                        _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace),
-                        workspace.numel() * workspace.element_size(), _stream(stream)))
+                        _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
     return dq, dk, dv
 
 

@@ -220,10 +220,14 @@ size_t mea_bwd_workspace_bytes(int B, int M, int Hq, unsigned bias_kind) {
   return 2 * one;
 }
 
-int mea_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-            void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D, float scale,
-            unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k, const float* alibi_slopes,
-            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D, float scale,
+             unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k, const float* alibi_slopes,
+             const uint8_t* block_mask, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return MEA_EINVAL;
@@ -239,6 +243,7 @@ int mea_bwd(const void* q, const void* k, const void* v, const void* out, const 
     if (seqstart_q == nullptr) return MEA_EINVAL;
     if (seqstart_k == nullptr && M != N) return MEA_EINVAL;
   }
+  if (varlen && block_mask != nullptr) return MEA_EINVAL;
   if (!mea_supported(dtype, D)) return MEA_EUNSUPPORTED;
   const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
   if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
@@ -261,6 +266,8 @@ int mea_bwd(const void* q, const void* k, const void* v, const void* out, const 
   p.seqstart_q = seqstart_q;
   p.seqstart_k = seqstart_k != nullptr ? seqstart_k : seqstart_q;
   p.slopes = alibi_slopes;
+  p.block_mask = block_mask;
+  p.nkb = (N + mea::kSparseBlock - 1) / mea::kSparseBlock;
   p.B = B;
   p.M = M;
   p.N = N;
@@ -308,6 +315,28 @@ int mea_bwd(const void* q, const void* k, const void* v, const void* out, const 
     if (rc != MEA_OK) return rc;
   }
   return mea::launch_bwd(dtype, D, p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mea_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D, float scale,
+            unsigned bias_kind, const int32_t* seqstart_q, const int32_t* seqstart_k, const float* alibi_slopes,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, M, N, Hq, Hkv, D, scale, bias_kind, seqstart_q, seqstart_k,
+                  alibi_slopes, nullptr, dtype, workspace, workspace_bytes, stream);
+}
+
+int mea_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int M, int N, int Hq, int Hkv, int D,
+                        float scale, unsigned bias_kind, const uint8_t* block_mask, const float* alibi_slopes,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_mask == nullptr) return MEA_EINVAL;
+  if ((bias_kind & MEA_MASK_BLOCKDIAG) != 0u) return MEA_EINVAL;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, M, N, Hq, Hkv, D, scale, bias_kind, nullptr, nullptr,
+                  alibi_slopes, block_mask, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {

@@ -27,7 +27,10 @@
 //     lane; P and dS, rounded, are the B operands of dV^T += dO^T P and
 //     dK^T += Q^T dS, with dO^T and Q^T from transpose reads.
 // Masks (causal bottom-right, segment ends) and ALiBi come from indices as in
-// the forward; blocks entirely above the diagonal are skipped.
+// the forward; blocks entirely above the diagonal are skipped. Under a
+// block-sparse mask (BS = 1, 64 x 64 blocks) each work-group walks only the
+// blocks some of its rows or keys need, and a wave skips the blocks that are
+// off for its own rows or keys.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -112,7 +115,7 @@ __device__ __forceinline__ int find_tile(const int32_t* st, int B, int total, in
 }
 
 // ---- dQ ------------------------------------------------------------------------
-template <typename T, int D, int CS, int AL>
+template <typename T, int D, int CS, int AL, int BS = 0>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWpe<D>, kBwdWpe<D>))) bwd_dq_kernel(const BwdParams p) {
   using MF = Mfma<T>;
   typedef typename MF::v8 v8;
@@ -231,15 +234,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int trow = (g16 >> 1) * 4 + (ll >> 2);
   const int tcol = (g16 & 1) * 16 + 4 * (ll & 3);
 
-  if (ntiles > 0) gload(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  // Block-sparse skip list over key blocks (K tiles are the mask's key blocks).
+  int qblo = 0, qbhi = -1, wqblk = -1;
+  if (BS) {
+    qblo = i0 >> 6;
+    qbhi = min(i0 + BM, M_s) - 1;
+    qbhi = qbhi >= i0 ? (qbhi >> 6) : qblo - 1;
+    wqblk = (wq0 < M_s) ? (wq0 >> 6) : -1;
+  }
+  auto next_tile = [&](int kt) {
+    if (BS) {
+      for (; kt < ntiles; ++kt) {
+        bool on = false;
+        for (int r = qblo; r <= qbhi; ++r) on |= p.block_mask[(long long)r * p.nkb + kt] != 0;
+        if (on) break;
+      }
+    }
+    return kt;
+  };
+  int kt0 = next_tile(0), nkt = 0;
+  if (kt0 < ntiles) gload(kt0);
+  for (int kt = kt0, n = 0; kt < ntiles; kt = nkt, ++n) {
+    const int buf = BS ? (n & 1) : (kt & 1);
+    nkt = next_tile(kt + 1);
     lstore(buf);
     __syncthreads();
-    if (kt + 1 < ntiles) gload(kt + 1);
+    if (nkt < ntiles) gload(nkt);
 
     const int key_base = kt * BN;
     if (key_base >= wkend) continue;
+    if (BS && (wqblk < 0 || p.block_mask[(long long)wqblk * p.nkb + kt] == 0)) continue;
     const uint16_t* Ks = smem + buf * 2 * TILE;
     const uint16_t* Vs = Ks + TILE;
 
@@ -322,7 +346,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
 }
 
 // ---- dK, dV ----------------------------------------------------------------------
-template <typename T, int D, int CS, int AL>
+template <typename T, int D, int CS, int AL, int BS = 0>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWpe<D>, kBwdWpe<D>))) bwd_dkdv_kernel(const BwdParams p) {
   using MF = Mfma<T>;
   typedef typename MF::v8 v8;
@@ -453,15 +477,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int tcol = (g16 & 1) * 16 + 4 * (ll & 3);
   const bool wave_has_keys = wj0 < N_s;
 
-  if (niter > 0) gload(0);
-  for (int it = 0; it < niter; ++it) {
-    const int buf = it & 1;
+  // Block-sparse skip list over query tiles (64 rows = one mask row): a tile
+  // is visited if either of the work-group's key blocks is on for it.
+  const int kblo = j0 >> 6;
+  const int kbhi = BS ? (min(j0 + BNK, N_s) - 1) >> 6 : kblo;
+  const int wkblk = wj0 >> 6;
+  auto next_it = [&](int it) {
+    if (BS) {
+      for (; it < niter; ++it) {
+        const int qrow = ((qfirst + (it % nqt) * BQ) >> 6);
+        bool on = false;
+        for (int c = kblo; c <= kbhi; ++c) on |= p.block_mask[(long long)qrow * p.nkb + c] != 0;
+        if (on) break;
+      }
+    }
+    return it;
+  };
+  int it0 = next_it(0), nit = 0;
+  if (it0 < niter) gload(it0);
+  for (int it = it0, n = 0; it < niter; it = nit, ++n) {
+    const int buf = BS ? (n & 1) : (it & 1);
+    nit = next_it(it + 1);
     lstore(buf);
     __syncthreads();
     const int hh = it / nqt;
     const int qt = it - hh * nqt;
-    if (it + 1 < niter) gload(it + 1);
+    if (nit < niter) gload(nit);
     if (!wave_has_keys) continue;
+    if (BS && p.block_mask[(long long)((qfirst + qt * BQ) >> 6) * p.nkb + wkblk] == 0) continue;
 
     const int h = g * p.group + hh;
     const float slope = ALIBI ? p.slopes[h] * kLog2e : 0.f;
@@ -563,7 +606,10 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
     if (blocks > 0) hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   }
   const dim3 gq(p.wg_per_xcd_q * 8), gk(p.wg_per_xcd_k * 8), blk(kWaves * 64);
-  if (!p.causal) {
+  if (p.block_mask != nullptr) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 2, 2, 1>), gk, blk, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, 2, 2, 1>), gq, blk, 0, stream, p);
+  } else if (!p.causal) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 0, 2>), gk, blk, 0, stream, p);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, 0, 2>), gq, blk, 0, stream, p);
   } else if (p.alibi) {

@@ -59,6 +59,8 @@ struct BwdParams {
   const int32_t* seqstart_q;
   const int32_t* seqstart_k;
   const float* slopes;
+  const uint8_t* block_mask;   // dense mode only, nullable: [ceil(M/64)][nkb] block-sparse mask
+  int nkb;
   int B, M, N, Hq, Hkv, group;
   int causal, varlen, alibi;
   float scale;           // as given

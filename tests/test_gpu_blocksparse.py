@@ -1,4 +1,4 @@
-"""Parity of the block-sparse forward (``mea_fwd_blocksparse``) with the fp64 oracle, on the GPU."""
+"""Parity of the block-sparse forward and backward (``mea_fwd_blocksparse``, ``mea_bwd_blocksparse``) with the fp64 oracle, on the GPU."""
 import numpy as np
 import pytest
 import torch
@@ -94,3 +94,43 @@ def test_band_global_full_size_sampled(mea):
         err = report(f"band_global h{h}", got[0, rows, h:h + 1], want, TOL["bf16"])
         assert err <= TOL["bf16"]
         assert np.max(np.abs(lse[0, h, rows].cpu().numpy() - wlse[0])) <= LSE_TOL["bf16"]
+
+
+BWD_CASES = [
+    # name, seed, B, M, N, Hq, Hkv, D, dtype, causal, alibi, density
+    ("bwd_ragged_m300_n260_d64_bf16_gqa", 5, 2, 300, 260, 4, 2, 64, "bf16", False, False, 0.4),
+    ("bwd_causal_alibi_m333_d128_fp16", 6, 1, 333, 333, 4, 4, 128, "fp16", True, True, 0.5),
+    ("bwd_causal_m512_d64_bf16", 7, 1, 512, 512, 4, 1, 64, "bf16", True, False, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: c[0])
+def test_blocksparse_bwd_parity(mea, case):
+    """Backward over a block-sparse mask (mea_bwd_blocksparse) against the
+    oracle, with the backward tests' tolerance; one query block and one key
+    block are fully off (their dq, resp. dk and dv, are exactly 0)."""
+    from test_gpu_bwd import C, U
+    name, seed, B, M, N, Hq, Hkv, D, dt, causal, alibi, dens = case
+    say(f"case blocksparse {name}")
+    c = inp.dense_case(seed, B, M, N, Hq, Hkv, D, dt)
+    bm = inp.random_block_mask(seed, -(-M // 64), -(-N // 64), dens)
+    bm[1, :] = 0
+    bm[:, 2] = 0
+    do = inp.normal_bits(seed + 500, (B, M, Hq, D), dt, 0)
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    q, k, v, dod = (dev(x, dt) for x in (c["q"], c["k"], c["v"], do))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    lse = torch.empty((B, Hq, M), dtype=torch.float32, device="cuda")
+    sl = None if slopes is None else f32(slopes)
+    m = _mask(bm)
+    out = mea.fwd_blocksparse(q, k, v, m, causal=causal, scale=scale, alibi_slopes=sl, lse=lse)
+    got = mea.bwd(q, k, v, out, dod, lse, causal=causal, scale=scale, alibi_slopes=sl, block_mask=m)
+    torch.cuda.synchronize()
+    want = orc.bwd(c["q"], c["k"], c["v"], do, dt, scale, causal=causal, alibi_slopes=slopes, block_mask=bm)
+    for label, g, w in zip(("dq", "dk", "dv"), got, want):
+        gh = host_f64(g)
+        tol = C * U[dt] * float(np.max(np.abs(w)))
+        assert report(f"{name} {label}", gh, w, tol) <= tol, label
+    assert np.all(host_f64(got[0])[:, 64:128] == 0), "dq of a query block with every block off"
+    assert np.all(host_f64(got[1])[:, 128:192] == 0) and np.all(host_f64(got[2])[:, 128:192] == 0), \
+        "dk, dv of a key block no query sees"
