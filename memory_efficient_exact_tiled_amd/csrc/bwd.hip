@@ -242,16 +242,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     qbhi = qbhi >= i0 ? (qbhi >> 6) : qblo - 1;
     wqblk = (wq0 < M_s) ? (wq0 >> 6) : -1;
   }
-  auto next_tile = [&](int kt) {
-    if (BS) {
-      for (; kt < ntiles; ++kt) {
-        bool on = false;
-        for (int r = qblo; r <= qbhi; ++r) on |= p.block_mask[(long long)r * p.nkb + kt] != 0;
-        if (on) break;
-      }
-    }
-    return kt;
+  __shared__ uint64_t skip_bits[4];
+  TileSkipList skip{skip_bits};
+  auto tile_on = [&](int kt) {
+    bool on = false;
+    for (int r = qblo; r <= qbhi; ++r) on |= p.block_mask[(long long)r * p.nkb + kt] != 0;
+    return on;
   };
+  auto next_tile = [&](int kt) { return BS ? skip.next_on(kt, ntiles, tile_on) : kt; };
   int kt0 = next_tile(0), nkt = 0;
   if (kt0 < ntiles) gload(kt0);
   for (int kt = kt0, n = 0; kt < ntiles; kt = nkt, ++n) {
@@ -482,13 +480,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int kblo = j0 >> 6;
   const int kbhi = BS ? (min(j0 + BNK, N_s) - 1) >> 6 : kblo;
   const int wkblk = wj0 >> 6;
+  __shared__ uint64_t skip_bits[4];
+  TileSkipList skip{skip_bits};
+  auto qtile_on = [&](int qt) {
+    const long long qrow = (qfirst + qt * BQ) >> 6;
+    bool on = false;
+    for (int c = kblo; c <= kbhi; ++c) on |= p.block_mask[qrow * p.nkb + c] != 0;
+    return on;
+  };
+  // Iterations run over (query head of the group, query tile); the skip list
+  // is over query tiles and the same for every head.
   auto next_it = [&](int it) {
     if (BS) {
-      for (; it < niter; ++it) {
-        const int qrow = ((qfirst + (it % nqt) * BQ) >> 6);
-        bool on = false;
-        for (int c = kblo; c <= kbhi; ++c) on |= p.block_mask[(long long)qrow * p.nkb + c] != 0;
-        if (on) break;
+      while (it < niter) {
+        const int hh = it / nqt;
+        const int qt = skip.next_on(it - hh * nqt, nqt, qtile_on);
+        if (qt < nqt) return hh * nqt + qt;
+        it = (hh + 1) * nqt;
       }
     }
     return it;

@@ -109,6 +109,44 @@ __device__ __forceinline__ uint32_t rows_bytes(long long n, long long row_bytes)
   return b > 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
 }
 
+// Work-group skip lists of block-sparse masks. The tiles [0, n) are
+// evaluated 256 at a time: each of the work-group's 256 threads tests one
+// tile with pred, a ballot per wave packs the results into a 256-bit set in
+// LDS, and the next tile that is on is then found with bit scans. Every
+// thread must call next_on with the same arguments (it holds barriers).
+struct TileSkipList {
+  uint64_t* lds;      // 4 words of LDS
+  int win = -1;       // window (tile / 256) held in bits
+  uint64_t bits[4];
+
+  template <typename Pred>
+  __device__ __forceinline__ int next_on(int t, int n, Pred pred) {
+    while (t < n) {
+      const int w = t >> 8;
+      if (w != win) {
+        __syncthreads();                        // readers of the previous window are done
+        const int tt = (w << 8) + (int)threadIdx.x;
+        const unsigned long long b = __ballot(tt < n && pred(tt));
+        if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = b;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bits[i] = lds[i];
+        win = w;
+      }
+      const int pos = t & 255;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < (pos >> 6)) continue;
+        uint64_t m = bits[i];
+        if (i == (pos >> 6)) m &= ~0ull << (pos & 63);
+        if (m != 0) return (w << 8) + i * 64 + __builtin_ctzll(m);
+      }
+      t = (w + 1) << 8;
+    }
+    return n;
+  }
+};
+
 // 2^x on the transcendental unit (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -240,16 +240,14 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
     qbhi = qbhi >= i0 ? (qbhi >> 6) : qblo - 1;
     wqblk = (wq0 < M_s) ? (wq0 >> 6) : -1;
   }
-  auto next_tile = [&](int it) {
-    if (BS) {
-      for (; it < ntiles; ++it) {
-        bool on = false;
-        for (int r = qblo; r <= qbhi; ++r) on |= p.block_mask[(long long)r * p.nkb + it] != 0;
-        if (on) break;
-      }
-    }
-    return it;
+  __shared__ uint64_t skip_bits[4];
+  TileSkipList skip{skip_bits};
+  auto tile_on = [&](int kt) {
+    bool on = false;
+    for (int r = qblo; r <= qbhi; ++r) on |= p.block_mask[(long long)r * p.nkb + kt] != 0;
+    return on;
   };
+  auto next_tile = [&](int it) { return BS ? skip.next_on(it, ntiles, tile_on) : it; };
   int it0 = next_tile(0), nit = 0;
   if (it0 < ntiles) gload(rev ? ntiles - 1 - it0 : it0);
   for (int it = it0, n = 0; it < ntiles; it = nit, ++n) {
@@ -419,8 +417,11 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
+  // Block-sparse launches use the 128-row work-group: the work-group walks
+  // the union of its query blocks' key blocks, which a smaller work-group
+  // keeps closer to what each wave needs.
   if (D == 64)
-    return (p.causal && p.block_mask == nullptr) ? launch_typed<T, 64, 1, true>(p, stream)
+    return (p.causal || p.block_mask != nullptr) ? launch_typed<T, 64, 1, true>(p, stream)
                                                  : launch_typed<T, 64, 2, false>(p, stream);
   return p.causal ? launch_typed<T, 128, 1, true>(p, stream) : launch_typed<T, 128, 1, false>(p, stream);
 }
@@ -428,7 +429,7 @@ hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 int fwd_block_m(int D, bool causal, bool block_sparse) {
-  if (D == 64) return (causal && !block_sparse) ? FwdShape<64, 1>::BM : FwdShape<64, 2>::BM;
+  if (D == 64) return (causal || block_sparse) ? FwdShape<64, 1>::BM : FwdShape<64, 2>::BM;
   return FwdShape<128, 1>::BM;
 }
 
