@@ -409,6 +409,8 @@ def main():
             "bound": "mfma", "achieved": round(tflops["bwd_noncausal"], 2), "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops["bwd_noncausal"] / PEAK_MFMA_TFLOPS, 4),
             "kernel": "bwd_prep + bwd_dkdv + bwd_dq <bf16,64> (non-causal)",
+            "traffic": traffic_for(traffic, "bwd_prep_kernelIDF16bLi64", "bwd_dkdv_kernelIDF16bLi64ELi0ELi2ELi0",
+                                   "bwd_dq_kernelIDF16bLi64ELi0ELi2ELi0"),
             "avg_launch_us": round(ms["bwd_noncausal"] * 1e3, 2),
             "algorithmic_flops": flops_all["bwd_noncausal"],
         },
