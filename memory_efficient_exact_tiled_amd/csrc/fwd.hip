@@ -32,7 +32,12 @@
 //   * causal and block-diagonal masks are index predicates evaluated only on
 //     blocks that straddle the diagonal or the segment end; blocks entirely
 //     above the diagonal are never visited (per work-group) or computed (per
-//     wave); ALiBi is computed from the indices;
+//     wave); ALiBi is computed from the indices. Under the causal mask the
+//     ALiBi bias of a key block is linear in the key's index within the block,
+//     so it is added by the score MFMA itself: one more k-step whose K column
+//     is that index (exact in 16-bit floats) and whose Q column is slope /
+//     scale split into two 16-bit parts; what is left per (row, block) is a
+//     constant folded into the exponent's offset;
 //   * grouped-query attention: query head h reads KV head h / (Hq / Hkv) in
 //     place; the heads sharing a KV head are adjacent in the launch order;
 //   * block-sparse masks (64 x 64 blocks of query rows and keys): the
@@ -174,6 +179,28 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
                                : zero_v8<T>();
   }
 
+  // Causal ALiBi through the MFMA (see the header): A rows = keys of the
+  // block (index kb * 32 + l32 in lanes with hi = 0, twice), B = slope / scale
+  // as hi + lo parts in lanes with hi = 0; zeros elsewhere.
+  v8 kx[2], qx;
+  if constexpr (CS == 1 && AL == 1) {
+    const float r = slope / c;                    // slope and c both in log2 units
+    const T rh = (T)r;
+    const T rl = (T)(r - (float)rh);
+    qx = zero_v8<T>();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) kx[kb] = zero_v8<T>();
+    if (hi == 0) {
+      qx[0] = rh;
+      qx[1] = rl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        kx[kb][0] = (T)(float)(kb * 32 + l32);
+        kx[kb][1] = (T)(float)(kb * 32 + l32);
+      }
+    }
+  }
+
   f32x16 o[QB][DB];
   float m_run[QB], l_run[QB];
 #pragma unroll
@@ -281,6 +308,10 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = MF::mma32(kf, qf[qb][st], s[qb][kb]);
       }
+      if constexpr (CS == 1 && AL == 1) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = MF::mma32(kx[kb], qx, s[qb][kb]);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -289,29 +320,40 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qi = wq0 + qb * 32 + l32;
-      float cc = c;
-      if (ALIBI || need_mask) {
+      float cc = c, bb = 0.f;   // exponent of P = s * cc + bb - (running max)
+      if constexpr (CS == 1 && AL == 1) {
+        // s already holds slope/scale * (key - key_base); the rest of the bias,
+        // -slope * (query position - key_base), is constant per row and block.
+        // Under the causal rule every allowed key is inside the segment.
+        bb = -slope * (float)(qi + off - key_base);
+        if (need_mask) {
+          const int lim_c = qi + off - key_base - hi * 4;   // kr <= lim_c : causal
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
+              s[qb][kb][r] = (kr <= lim_c) ? fmaf(s[qb][kb][r], c, bb) : -INFINITY;
+            }
+          cc = 1.f;
+          bb = 0.f;
+        }
+      } else if (ALIBI || need_mask) {
         // Explicit scores in log2 units: scale, ALiBi from indices, mask.
         const int rel = key_base + hi * 4;           // key = rel + kr
         const int lim_n = N_s - rel;                 // kr <  lim_n : inside the segment
         const int lim_c = CAUSAL ? (qi + off - rel) : 0x7fffffff;  // kr <= lim_c : causal
         const float dist0 = (float)(qi + off - rel); // query position - key, at kr = 0
-        const float nb = -slope * dist0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
-            float x;
-            if constexpr (CS == 1 && AL == 1) {
-              // Allowed keys have dist0 - kr >= 0, so |.| is not needed.
-              x = fmaf(s[qb][kb][r], c, fmaf(slope, (float)kr, nb));
-              if (need_mask) x = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
-            } else {
-              x = s[qb][kb][r] * c;
-              if (ALIBI) x -= slope * fabsf(dist0 - (float)kr);
-              x = (kr < lim_n && kr <= lim_c) ? x : -INFINITY;
-            }
+            float x = s[qb][kb][r] * c;
+            if (ALIBI) x -= slope * fabsf(dist0 - (float)kr);
+            // Under a compile-time causal mask every allowed key of a real row
+            // is inside the segment, so only the causal bound is tested.
+            x = ((CS == 1 || kr < lim_n) && kr <= lim_c) ? x : -INFINITY;
             s[qb][kb][r] = x;
           }
         cc = 1.f;
@@ -325,7 +367,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       }
-      const float mt = mx * cc;
+      const float mt = fmaf(mx, cc, bb);
       if (__any(mt > m_run[qb] + kRescaleThreshold)) {
         const float mn = fmaxf(m_run[qb], mt);
         const float alpha = fast_exp2(m_run[qb] - (mn == -INFINITY ? 0.f : mn));
@@ -340,7 +382,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(fmaf(s[qb][kb][r], cc, -mu));
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(fmaf(s[qb][kb][r], cc, bb - mu));
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
