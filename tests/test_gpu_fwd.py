@@ -107,6 +107,14 @@ VARLEN = [
     ("ragged_segments_noncausal_d64_fp16", [5, 300, 1, 129], 4, 4, 64, "fp16", False, False),
     ("ragged_segments_noncausal_alibi", [40, 100, 3], 4, 1, 64, "bf16", False, True),
     ("one_segment", [513], 2, 1, 128, "fp16", True, False),
+    # the launch order of packed batches: one segment per lane up to 64
+    # segments (exactly 64 here, some empty), a serial scan beyond (70), and
+    # the head split across XCDs only when Hq is a multiple of 8 (6 here)
+    ("segments_64_causal_hq8", [0, 3] + [int(x) for x in np.random.default_rng(5).integers(1, 150, 61)] + [0],
+     8, 2, 64, "bf16", True, False),
+    ("segments_70_causal_alibi", [int(x) for x in np.random.default_rng(6).integers(0, 120, 70)],
+     8, 4, 128, "bf16", True, True),
+    ("segments_hq6_noncausal", [77, 0, 200, 31, 129], 6, 2, 64, "fp16", False, False),
 ]
 
 
