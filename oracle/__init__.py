@@ -7,9 +7,11 @@ it, shares no code with it and has no CPU fallback.
 
 Every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` against library routines, closed forms and the
-invariants the pages fix. One reading is parity unpinned by the pages: the
-form of ALiBi without a causal mask (it is tested against the stated reading
-only).
+invariants the pages fix. Two readings are parity unpinned by the pages: the
+form of ALiBi without a causal mask, and the block-sparse mask (64 x 64
+blocks ANDed with the causal rule; the pages name a block-sparse variant
+without defining it). Both are tested against the stated reading only (the
+block mask against torch SDPA with the element mask the blocks expand to).
 """
 from .attention import (  # noqa: F401
     BLOCK,
