@@ -90,6 +90,21 @@ def varlen_case(seed: int, lengths, Hq: int, Hkv: int, D: int, dtype: str) -> di
     }
 
 
+def varlen_cross_case(seed: int, q_lengths, k_lengths, Hq: int, Hkv: int, D: int, dtype: str) -> dict:
+    """Packed batch whose query and key segments differ in length (segment s
+    of q attends to segment s of k): q ``[1,Tq,Hq,D]``, k and v ``[1,Tk,Hkv,D]``,
+    ``seqstart_q`` and ``seqstart_k`` int32 ``[nseq+1]``."""
+    sq, sk = seqstart(q_lengths), seqstart(k_lengths)
+    return {
+        "q": normal_bits(seed, (1, int(sq[-1]), Hq, D), dtype, _Q),
+        "k": normal_bits(seed, (1, int(sk[-1]), Hkv, D), dtype, _K),
+        "v": normal_bits(seed, (1, int(sk[-1]), Hkv, D), dtype, _V),
+        "seqstart_q": sq,
+        "seqstart_k": sk,
+        "dtype": dtype,
+    }
+
+
 def alibi_slopes(Hq: int) -> np.ndarray:
     """Per-query-head ALiBi slopes ``2^(-8(h+1)/Hq)``, h = 0..Hq-1, as float32."""
     h = np.arange(Hq, dtype=np.float64)

@@ -523,6 +523,34 @@ def check_blocksparse_masked_blocks_do_not_matter(orc):
     assert not np.array_equal(o[:, 128:], o2[:, 128:]), "query block 2 must see key blocks 1 and 3"
     assert np.all(o[:, 64:128] == 0) and np.all(np.isneginf(lse[:, :, 64:128])), "empty query block"
 
+
+def check_blockdiag_cross_segments(orc):
+    """Packed cross-attention (query segment s sees key segment s, lengths
+    differ, some empty) == each segment's own dense attention, forward and
+    backward, with the bottom-right causal alignment per segment."""
+    ql, kl = [5, 9, 0, 4, 3], [8, 3, 6, 4, 0]
+    c = inp.varlen_cross_case(50, ql, kl, 4, 2, 8, "bf16")
+    sq, sk = c["seqstart_q"], c["seqstart_k"]
+    do = inp.normal_bits(150, c["q"].shape, "bf16", 0)
+    for causal, slopes in [(False, None), (True, inp.alibi_slopes(4))]:
+        o, lse = orc.fwd(c["q"], c["k"], c["v"], "bf16", 0.3, causal=causal, seqstart_q=sq, seqstart_k=sk,
+                         alibi_slopes=slopes)
+        g = orc.bwd(c["q"], c["k"], c["v"], do, "bf16", 0.3, causal=causal, seqstart_q=sq, seqstart_k=sk,
+                    alibi_slopes=slopes)
+        for s_ in range(len(ql)):
+            a, b, e, f = sq[s_], sq[s_ + 1], sk[s_], sk[s_ + 1]
+            if b > a and f > e:
+                os_, ls_ = orc.fwd(c["q"][:, a:b], c["k"][:, e:f], c["v"][:, e:f], "bf16", 0.3, causal=causal,
+                                   alibi_slopes=slopes)
+                gs = orc.bwd(c["q"][:, a:b], c["k"][:, e:f], c["v"][:, e:f], do[:, a:b], "bf16", 0.3,
+                             causal=causal, alibi_slopes=slopes)
+                assert np.array_equal(o[:, a:b], os_) and np.array_equal(lse[:, :, a:b], ls_), ("cross fwd", s_)
+                assert np.array_equal(g[0][:, a:b], gs[0]) and np.array_equal(g[1][:, e:f], gs[1]) \
+                    and np.array_equal(g[2][:, e:f], gs[2]), ("cross bwd", s_)
+            else:   # no keys or no queries: zero output / zero gradients
+                assert np.all(o[:, a:b] == 0) and np.all(g[0][:, a:b] == 0), ("cross empty q", s_)
+                assert np.all(g[1][:, e:f] == 0) and np.all(g[2][:, e:f] == 0), ("cross empty k", s_)
+
 ALL_CHECKS = [
     check_sdpa_nomask,
     check_sdpa_causal_square,
@@ -553,4 +581,5 @@ ALL_CHECKS = [
     check_blocksparse_sdpa_bool_mask,
     check_blocksparse_all_on_is_dense,
     check_blocksparse_masked_blocks_do_not_matter,
+    check_blockdiag_cross_segments,
 ]

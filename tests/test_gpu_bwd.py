@@ -210,3 +210,27 @@ def test_bwd_rejects_bad_workspace(mea):
     with pytest.raises(mea.MeaError) as e:
         mea.bwd(q, k, v, out, out, lse, workspace=small)
     assert e.value.status == mea.MEA_EWORKSPACE
+
+
+def test_varlen_cross_segments_bwd(mea):
+    """Backward of packed cross-attention (seqstart_k != seqstart_q), causal
+    with ALiBi and GQA; key segments no query sees get dk = dv = 0."""
+    say("case bwd cross segments")
+    ql, kl = [130, 64, 0, 300, 7, 200], [200, 64, 50, 129, 7, 0]
+    c = inp.varlen_cross_case(41, ql, kl, 8, 2, 128, "bf16")
+    do = inp.normal_bits(541, c["q"].shape, "bf16", 0)
+    dt, Hq = "bf16", 8
+    q, k, v, dod = (dev(x, dt) for x in (c["q"], c["k"], c["v"], do))
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    slopes = inp.alibi_slopes(Hq)
+    sq, sk = i32(c["seqstart_q"]), i32(c["seqstart_k"])
+    lse = torch.empty((Hq, int(c["seqstart_q"][-1])), dtype=torch.float32, device="cuda")
+    out = mea.fwd(q, k, v, causal=True, scale=scale, seqstart_q=sq, seqstart_k=sk, alibi_slopes=f32(slopes), lse=lse)
+    got = mea.bwd(q, k, v, out, dod, lse, causal=True, scale=scale, seqstart_q=sq, seqstart_k=sk,
+                  alibi_slopes=f32(slopes))
+    torch.cuda.synchronize()
+    want = orc.bwd(c["q"], c["k"], c["v"], do, dt, scale, causal=True, seqstart_q=c["seqstart_q"],
+                   seqstart_k=c["seqstart_k"], alibi_slopes=slopes)
+    _check("bwd cross segments", got, want, dt)
+    e, f = int(c["seqstart_k"][2]), int(c["seqstart_k"][3])      # key segment 2: its query segment is empty
+    assert np.all(host_f64(got[1])[:, e:f] == 0) and np.all(host_f64(got[2])[:, e:f] == 0)

@@ -201,3 +201,34 @@ def test_no_nan_from_neighbours(mea):
     want, _ = orc.fwd(c["q"][:, :T], c["k"][:, :T], c["v"][:, :T], "bf16", 0.125, causal=True,
                       seqstart_q=st[:3])
     assert report("nan neighbours", got, want[0], TOL["bf16"]) <= TOL["bf16"]
+
+
+CROSS = [
+    # name, q lengths, k lengths, Hq, Hkv, D, dtype, causal, alibi
+    ("cross_causal_alibi_d128", [130, 64, 0, 300, 7, 200], [200, 64, 50, 129, 7, 0], 8, 2, 128, "bf16", True, True),
+    ("cross_noncausal_d64_fp16", [1, 257, 90], [333, 5, 0], 4, 4, 64, "fp16", False, False),
+]
+
+
+@pytest.mark.parametrize("case", CROSS, ids=lambda c: c[0])
+def test_varlen_cross_segments(mea, case):
+    """Packed cross-attention: query segment s attends to key segment s of a
+    different length (seqstart_k != seqstart_q), bottom-right causal per
+    segment, empty query or key segments."""
+    name, ql, kl, Hq, Hkv, D, dt, causal, alibi = case
+    say(f"case {name}")
+    c = inp.varlen_cross_case(40, ql, kl, Hq, Hkv, D, dt)
+    q, k, v = dev(c["q"], dt), dev(c["k"], dt), dev(c["v"], dt)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    lse = torch.full((Hq, int(c["seqstart_q"][-1])), 7.0, dtype=torch.float32, device="cuda")
+    out = mea.fwd(q, k, v, causal=causal, scale=scale, seqstart_q=i32(c["seqstart_q"]),
+                  seqstart_k=i32(c["seqstart_k"]), alibi_slopes=None if slopes is None else f32(slopes), lse=lse)
+    torch.cuda.synchronize()
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=causal, seqstart_q=c["seqstart_q"],
+                         seqstart_k=c["seqstart_k"], alibi_slopes=slopes)
+    assert report(name, host_f64(out), want, TOL[dt]) <= TOL[dt]
+    got_lse = lse.cpu().numpy()
+    fin = np.isfinite(wlse[0])
+    assert np.array_equal(np.isfinite(got_lse), fin), "lse -inf pattern"
+    assert np.max(np.abs(got_lse[fin] - wlse[0][fin]), initial=0.0) <= LSE_TOL[dt]
