@@ -37,7 +37,8 @@
 //     so it is added by the score MFMA itself: one more k-step whose K column
 //     is that index (exact in 16-bit floats) and whose Q column is slope /
 //     scale split into two 16-bit parts; what is left per (row, block) is a
-//     constant folded into the exponent's offset;
+//     constant folded into the exponent's offset (heads with steep slopes,
+//     where fp32 accumulation would blur the scores, add the bias per score);
 //   * grouped-query attention: query head h reads KV head h / (Hq / Hkv) in
 //     place; the heads sharing a KV head are adjacent in the launch order;
 //   * block-sparse masks (64 x 64 blocks of query rows and keys): the
@@ -86,9 +87,16 @@ struct FwdShape {
 // specialise both; the dense launch reads both at run time, which the
 // compiler schedules better than the fully specialised form. BS = 1 reads a
 // block-sparse mask (p.block_mask).
+// Waves per SIMD of an instantiation: the causal ALiBi form carries both the
+// folded and the explicit bias, which needs the register budget of two waves.
+template <int D, int QB, int CS, int AL>
+constexpr int fwd_wpe() {
+  return (CS == 1 && AL == 1) ? 2 : FwdShape<D, QB>::WPE;
+}
+
 template <typename T, int D, int QB_, int CS, int AL, int BS = 0>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE))) fwd_kernel(const FwdParams p) {
+__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, QB_, CS, AL>(), fwd_wpe<D, QB_, CS, AL>()))) fwd_kernel(const FwdParams p) {
   using S = FwdShape<D, QB_>;
   using MF = Mfma<T>;
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
@@ -183,10 +191,20 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   // block (index kb * 32 + l32 in lanes with hi = 0, twice), B = slope / scale
   // as hi + lo parts in lanes with hi = 0; zeros elsewhere.
   v8 kx[2], qx;
+  // The fold is exact to fp32 accumulation: the bias term kl * r rounds with
+  // the score at about 63 * |slope| * 2^-24 (log2 units), independent of the
+  // scale. Heads with |slope| > 16 (log2 units) take the explicit bias instead.
+  const bool fold = (CS == 1 && AL == 1) && fabsf(slope) <= 16.f;
   if constexpr (CS == 1 && AL == 1) {
-    const float r = slope / c;                    // slope and c both in log2 units
-    const T rh = (T)r;
-    const T rl = (T)(r - (float)rh);
+    // r = slope / scale (both in log2 units). fp16 holds at most 65504, so a
+    // power of two 2^e moves from the Q column to the K column (index * 2^e
+    // stays exact for index < 64 and e <= 10).
+    const float r = fold ? slope / c : 0.f;
+    int e = 0;
+    if constexpr (__is_same(T, _Float16)) e = min(max(ilogbf(fabsf(r)) - 14, 0), 10);
+    const float rs = ldexpf(r, -e);
+    const T rh = (T)rs;
+    const T rl = (T)(rs - (float)rh);
     qx = zero_v8<T>();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) kx[kb] = zero_v8<T>();
@@ -195,8 +213,8 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
       qx[1] = rl;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        kx[kb][0] = (T)(float)(kb * 32 + l32);
-        kx[kb][1] = (T)(float)(kb * 32 + l32);
+        kx[kb][0] = (T)ldexpf((float)(kb * 32 + l32), e);
+        kx[kb][1] = kx[kb][0];
       }
     }
   }
@@ -326,14 +344,19 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
         // -slope * (query position - key_base), is constant per row and block.
         // Under the causal rule every allowed key is inside the segment.
         bb = -slope * (float)(qi + off - key_base);
-        if (need_mask) {
+        if (need_mask || !fold) {
           const int lim_c = qi + off - key_base - hi * 4;   // kr <= lim_c : causal
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
-              s[qb][kb][r] = (kr <= lim_c) ? fmaf(s[qb][kb][r], c, bb) : -INFINITY;
+              // Unfolded, the bias comes from the exact integer distance
+              // (query position - key = lim_c - kr): a product of the large
+              // per-block part and a separate in-block part would not cancel
+              // exactly at steep slopes.
+              const float bias = fold ? bb : -slope * (float)(lim_c - kr);
+              s[qb][kb][r] = (!need_mask || kr <= lim_c) ? fmaf(s[qb][kb][r], c, bias) : -INFINITY;
             }
           cc = 1.f;
           bb = 0.f;
@@ -443,29 +466,27 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   }
 }
 
-template <typename T, int D, int QB, bool CAUSAL>
-hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
-  const int grid = p.wg_per_xcd * 8;
-  if (p.block_mask != nullptr)
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 2, 2, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
-  else if (!CAUSAL)
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 2, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
-  else if (p.alibi)
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 1, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, 1, 0>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+template <typename T, int D, int QB, int CS, int AL, int BS>
+hipError_t launch_k(const FwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_kernel<T, D, QB, CS, AL, BS>), dim3(p.wg_per_xcd * 8), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+// Launch shapes (fwd_block_m must agree): the dense launch runs QB=2 at D=64;
+// causal and block-sparse launches run QB=1 (128-row work-groups), which
+// halves the rows a diagonal block masks off and keeps the skip list of a
+// work-group close to what each wave needs.
+template <typename T, int D>
+hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  constexpr int kDenseQB = D == 64 ? 2 : 1;
+  if (p.block_mask != nullptr) return launch_k<T, D, 1, 2, 2, 1>(p, stream);
+  if (!p.causal) return launch_k<T, D, kDenseQB, 2, 2, 0>(p, stream);
+  return p.alibi ? launch_k<T, D, 1, 1, 1, 0>(p, stream) : launch_k<T, D, 1, 1, 0, 0>(p, stream);
 }
 
 template <typename T>
 hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
-  // Block-sparse launches use the 128-row work-group: the work-group walks
-  // the union of its query blocks' key blocks, which a smaller work-group
-  // keeps closer to what each wave needs.
-  if (D == 64)
-    return (p.causal || p.block_mask != nullptr) ? launch_typed<T, 64, 1, true>(p, stream)
-                                                 : launch_typed<T, 64, 2, false>(p, stream);
-  return p.causal ? launch_typed<T, 128, 1, true>(p, stream) : launch_typed<T, 128, 1, false>(p, stream);
+  return D == 64 ? launch_d<T, 64>(p, stream) : launch_d<T, 128>(p, stream);
 }
 
 }  // namespace

@@ -232,3 +232,19 @@ def test_varlen_cross_segments(mea, case):
     fin = np.isfinite(wlse[0])
     assert np.array_equal(np.isfinite(got_lse), fin), "lse -inf pattern"
     assert np.max(np.abs(got_lse[fin] - wlse[0][fin]), initial=0.0) <= LSE_TOL[dt]
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_causal_alibi_extreme_slopes(mea, dt):
+    """Causal ALiBi with slope / scale from 0.4 to 1e7: the bias the score
+    MFMA adds must stay finite and exact enough in either 16-bit type."""
+    say(f"case causal alibi extreme slopes {dt}")
+    c = inp.dense_case(77, 2, 200, 200, 4, 2, 64, dt)
+    slopes = np.float32([2.0 ** -8, 1.0, 300.0, 1.0e5])
+    scale = 0.01
+    out, lse, _ = _run(mea, c, dt, causal=True, slopes=slopes, scale=scale, with_lse=True)
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=True, alibi_slopes=slopes)
+    got = host_f64(out)
+    assert np.all(np.isfinite(got))
+    assert report(f"extreme slopes {dt}", got, want, TOL[dt]) <= TOL[dt]
+    assert np.max(np.abs(lse.cpu().numpy() - wlse)) <= LSE_TOL[dt] * max(1.0, float(np.max(np.abs(wlse))) * 2 ** -11)
