@@ -87,16 +87,9 @@ struct FwdShape {
 // specialise both; the dense launch reads both at run time, which the
 // compiler schedules better than the fully specialised form. BS = 1 reads a
 // block-sparse mask (p.block_mask).
-// Waves per SIMD of an instantiation: the causal ALiBi form carries both the
-// folded and the explicit bias, which needs the register budget of two waves.
-template <int D, int QB, int CS, int AL>
-constexpr int fwd_wpe() {
-  return (CS == 1 && AL == 1) ? 2 : FwdShape<D, QB>::WPE;
-}
-
 template <typename T, int D, int QB_, int CS, int AL, int BS = 0>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, QB_, CS, AL>(), fwd_wpe<D, QB_, CS, AL>()))) fwd_kernel(const FwdParams p) {
+__attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE))) fwd_kernel(const FwdParams p) {
   using S = FwdShape<D, QB_>;
   using MF = Mfma<T>;
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
@@ -346,16 +339,19 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, QB_, CS, AL>(), fwd_wpe<D, QB_, CS
         bb = -slope * (float)(qi + off - key_base);
         if (need_mask || !fold) {
           const int lim_c = qi + off - key_base - hi * 4;   // kr <= lim_c : causal
+          // Unfolded, the bias comes from the exact distance (query position -
+          // key = lim_c - kr, exact as a float difference of integers below
+          // 2^24): a product of the large per-block part and a separate
+          // in-block part would not cancel exactly at steep slopes.
+          const float dl = (float)lim_c;
+          const float sl = fold ? 0.f : slope;
+          const float b0 = fold ? bb : 0.f;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kr = kb * 32 + (r >> 2) * 8 + (r & 3);
-              // Unfolded, the bias comes from the exact integer distance
-              // (query position - key = lim_c - kr): a product of the large
-              // per-block part and a separate in-block part would not cancel
-              // exactly at steep slopes.
-              const float bias = fold ? bb : -slope * (float)(lim_c - kr);
+              const float bias = fmaf(sl, (float)kr - dl, b0);
               s[qb][kb][r] = (!need_mask || kr <= lim_c) ? fmaf(s[qb][kb][r], c, bias) : -INFINITY;
             }
           cc = 1.f;
