@@ -102,6 +102,13 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
+// LDS DMA (buffer_load_dwordx4 ... lds): lane i of the wave copies 16 bytes
+// from the buffer at voff to lds_dst + 16 * i; lds_dst is wave-uniform. The
+// copy completes asynchronously (vmcnt), ahead of any barrier that publishes it.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
+}
+
 // Byte count of rows [0, n) of a row-major tensor, clamped to the 32-bit
 // range of a buffer resource (n <= 0 gives 0).
 __device__ __forceinline__ uint32_t rows_bytes(long long n, long long row_bytes) {

@@ -13,10 +13,12 @@
 //     segment, query head); wave w owns 32 * QB consecutive rows; two waves
 //     (three at QB=1, D=64) share each SIMD, so one wave's softmax overlaps
 //     another's matrix-core work; MFMA phases run at raised wave priority;
-//   * K/V blocks of BN = 64 keys are copied HBM -> registers -> LDS with
-//     buffer loads whose resource ends at the segment's last key (rows past
-//     it read as zeros), double buffered so one barrier per block suffices;
-//     the next block's loads are in flight while the current one is computed;
+//   * K/V blocks of BN = 64 keys are copied to LDS with buffer loads whose
+//     resource ends at the segment's last key (rows past it read as zeros):
+//     straight into LDS (LDS DMA) at D=128, through registers at D=64 (the
+//     faster of the two for each); double buffered so one barrier per block
+//     suffices, with the next block's copies in flight during the current
+//     block's compute;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
 //     registers for the whole kernel). With this orientation each lane holds
 //     one query's scores for 32 of the 64 keys, so the row max needs a single
@@ -225,6 +227,9 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   }
 
   // ---- K/V staging ---------------------------------------------------------
+  // D=64: K/V staging through registers (HBM -> VGPRs -> LDS), which measured
+  // faster there than the LDS DMA the D=128 kernels use.
+  constexpr bool kDma = D == 128;
   uint4 kst[NLD], vst[NLD];
   const uint32_t row_bytes = (uint32_t)p.kv_rstride * 2u;
   uint32_t ld_off[NLD];
@@ -253,6 +258,49 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
       const int cc = (ch - r * CPR) * 8;
       *reinterpret_cast<uint4*>(ks + r * LDSK + cc) = kst[i];
       *reinterpret_cast<uint4*>(ks + TILE + r * LDS + cc) = vst[i];
+    }
+  };
+
+  // D=128: K/V staging by LDS DMA (buffer_load ... lds). One wave-instruction
+  // writes 64 consecutive 16-byte chunks of a padded block, lane i the i-th;
+  // wave w issues instructions w, w + 4, ... of the K block (LDSK / 8 chunks
+  // per row) and of the V block (LDS / 8). Pad chunks re-load their row's
+  // first chunk (an in-range address). Rows past the segment end read as
+  // zeros (buffer range).
+  constexpr int KCH = LDSK / 8, VCH = LDS / 8;
+  constexpr int NKI = kBN * KCH / 64, NVI = kBN * VCH / 64;
+  constexpr int MKI = (NKI + kWaves - 1) / kWaves, MVI = (NVI + kWaves - 1) / kWaves;
+  static_assert(kBN * KCH % 64 == 0 && kBN * VCH % 64 == 0, "blocks must be whole wave-instructions");
+  uint32_t koffs[MKI], voffs[MVI];
+#pragma unroll
+  for (int i = 0; i < MKI; ++i) {
+    const int q = (wave + i * kWaves) * 64 + lane;
+    const int row = q / KCH, cch = q - row * KCH;
+    koffs[i] = (uint32_t)row * row_bytes + (cch < D / 8 ? (uint32_t)cch * 16u : 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < MVI; ++i) {
+    const int q = (wave + i * kWaves) * 64 + lane;
+    const int row = q / VCH, cch = q - row * VCH;
+    voffs[i] = (uint32_t)row * row_bytes + (cch < D / 8 ? (uint32_t)cch * 16u : 0u);
+  }
+  auto dma = [&](int kt, int buf) {
+    const uint32_t bytes = rows_bytes(N_s - kt * kBN, row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + koff + (long long)kt * kBN * p.kv_rstride, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + koff + (long long)kt * kBN * p.kv_rstride, bytes);
+    uint16_t* kdst = smem + buf * 2 * TILE;
+    uint16_t* vdst = kdst + TILE;
+#pragma unroll
+    for (int i = 0; i < MKI; ++i) {
+      const int j = wave + i * kWaves;
+      if (j < NKI)
+        lds_dma16(rk, kdst + j * 512, koffs[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MVI; ++i) {
+      const int j = wave + i * kWaves;
+      if (j < NVI)
+        lds_dma16(rv, vdst + j * 512, voffs[i]);
     }
   };
 
@@ -287,14 +335,23 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   };
   auto next_tile = [&](int it) { return BS ? skip.next_on(it, ntiles, tile_on) : it; };
   int it0 = next_tile(0), nit = 0;
-  if (it0 < ntiles) gload(rev ? ntiles - 1 - it0 : it0);
+  if (it0 < ntiles) {
+    if constexpr (kDma) dma(rev ? ntiles - 1 - it0 : it0, 0);
+    else gload(rev ? ntiles - 1 - it0 : it0);
+  }
   for (int it = it0, n = 0; it < ntiles; it = nit, ++n) {
     const int kt = rev ? ntiles - 1 - it : it;
-    const int buf = BS ? (n & 1) : (it & 1);
+    const int buf = n & 1;
     nit = next_tile(it + 1);
-    lstore(buf);
-    __syncthreads();
-    if (nit < ntiles) gload(rev ? ntiles - 1 - nit : nit);
+    if constexpr (kDma) {
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's block copies have landed in LDS
+      __syncthreads();                 // ... and every wave's
+      if (nit < ntiles) dma(rev ? ntiles - 1 - nit : nit, buf ^ 1);
+    } else {
+      lstore(buf);
+      __syncthreads();
+      if (nit < ntiles) gload(rev ? ntiles - 1 - nit : nit);
+    }
 
     const int key_base = kt * kBN;
     if (key_base >= wkend) continue;   // the whole block is masked for this wave
