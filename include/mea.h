@@ -207,9 +207,11 @@ int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_n
 /*
  * mea_decode - one KV-cache decode step: each sequence's newest query
  * attends to all of its cached keys (its own key and value already
- * appended). Split-KV: the context is cut into fixed chunks, each chunk
- * yields a partial (row max, row sum, unnormalised output) for all query
- * heads of one KV head, and a combine kernel merges the partials by their
+ * appended). Split-KV: the cached keys of all sequences, laid end to end,
+ * are cut into equal spans (one per split work-group, at least
+ * mea_decode_chunk() keys each), each span yields one partial (row max, row
+ * sum, unnormalised output) per sequence it touches for all query heads of
+ * one KV head, and a combine kernel merges a sequence's partials by their
  * log-sum-exp. The step itself: "Transformer : comprendre l'entrainement et
  * l'inference" (briefia.fr), sections on prefill vs decode and the simple
  * KV cache; the single-query equivalence: "Transformerを実装して少し理解した
@@ -218,7 +220,9 @@ int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_n
  *
  *   q, out   [B, Hq, D]             (one query per sequence)
  *   kcache   [B, S_max, Hkv, D]     vcache same
- *   ctx_lens int32 device array [B], 0 <= ctx_lens[b] <= S_max. Slots
+ *   ctx_lens int32 device array [B], 0 <= ctx_lens[b] <= S_max (larger
+ *            values are clamped to S_max, negative ones to 0), and
+ *            B * S_max < 2^31 (else MEA_EINVAL). Slots
  *            >= ctx_lens[b] are never read and may hold anything (NaN).
  *            ctx_lens[b] == 0 gives out = 0.
  *   The query of sequence b sits at position ctx_lens[b]-1 (ALiBi distance
@@ -243,7 +247,8 @@ const char* mea_strerror(int status);
  * of supported kernels answers in the tutorial's setup section). */
 int mea_supported(int dtype, int D);
 
-/* Decode split-KV chunk length in keys (the granularity of the workspace). */
+/* Shortest span of keys of one decode split work-group (the granularity of
+ * the decode workspace). */
 int mea_decode_chunk(void);
 
 #ifdef __cplusplus

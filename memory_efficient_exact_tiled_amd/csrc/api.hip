@@ -339,13 +339,51 @@ int mea_bwd_blocksparse(const void* q, const void* k, const void* v, const void*
                   alibi_slopes, block_mask, dtype, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Decode workspace: the plan ([B + 2] int32: prefix sums of ctx, then the span
+// of keys per split work-group), then the partial outputs [B][Hq][nsplit][D]
+// and (max, sum) pairs [B][Hq][nsplit][2], each part 256-byte aligned. A
+// sequence is covered by at most ceil(S_max / kDecodeChunk) + 1 work-groups.
+struct DecLayout {
+  size_t plan, o, ml, total;
+  long long nsplit;
+};
+
+DecLayout dec_layout(int B, int Hq, int D, int S_max) {
+  DecLayout l{};
+  l.nsplit = ((long long)S_max + mea::kDecodeChunk - 1) / mea::kDecodeChunk + 1;
+  const size_t slots = (size_t)B * (size_t)Hq * (size_t)l.nsplit;
+  l.plan = ((size_t)(B + 2) * sizeof(int32_t) + 255) & ~(size_t)255;
+  l.o = (slots * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
+  l.ml = slots * 2 * sizeof(float);
+  l.total = l.plan + l.o + l.ml;
+  return l;
+}
+
+// Split work-groups of a decode launch: one per compute unit of the current
+// device (queried once per device).
+int decode_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {
   if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
-  const size_t nchunk = ((size_t)S_max + mea::kDecodeChunk - 1) / mea::kDecodeChunk;
-  const size_t slots = (size_t)B * (size_t)Hq * nchunk;
-  size_t o_bytes = slots * (size_t)D * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  return o_bytes + slots * 2 * sizeof(float);
+  return dec_layout(B, Hq, D, S_max).total;
 }
 
 int mea_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
@@ -358,13 +396,15 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   if (!(scale > 0.f) || !std::isfinite(scale)) return MEA_EINVAL;
   if (!mea_supported(dtype, D)) return MEA_EUNSUPPORTED;
   if ((long long)Hkv * D > 0x7fffffffLL) return MEA_EINVAL;
+  // Context prefix sums are int32 on the device.
+  if ((long long)B * (long long)S_max > 0x7fffffffLL) return MEA_EINVAL;
   const size_t need = mea_decode_workspace_bytes(B, Hq, D, S_max);
   if (workspace == nullptr || workspace_bytes < need) return MEA_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return MEA_EWORKSPACE;
-  const long long nchunk = ((long long)S_max + mea::kDecodeChunk - 1) / mea::kDecodeChunk;
+  const DecLayout lay = dec_layout(B, Hq, D, S_max);
   const int group = Hq / Hkv;
   const int nhb = (group + 15) / 16;
-  if (nchunk > 0x7fffffffLL || (long long)Hkv * nhb > 65535 || B > 65535) return MEA_EINVAL;
+  if (lay.nsplit > 0x7fffffffLL || (long long)Hkv * nhb > 65535 || B > 65535) return MEA_EINVAL;
 
   mea::DecParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -373,16 +413,17 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   p.ctx = ctx_lens;
   p.out = static_cast<uint16_t*>(out);
   p.slopes = alibi_slopes;
-  const size_t slots = (size_t)B * (size_t)Hq * (size_t)nchunk;
-  size_t o_bytes = (slots * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  char* ws = static_cast<char*>(workspace);
+  p.plan = reinterpret_cast<int*>(ws);
+  p.ws_o = reinterpret_cast<float*>(ws + lay.plan);
+  p.ws_ml = reinterpret_cast<float*>(ws + lay.plan + lay.o);
+  p.nsplit = (int)lay.nsplit;
+  p.grid = decode_grid();
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.group = group;
   p.S_max = S_max;
-  p.nchunk = (int)nchunk;
   p.nhb = nhb;
   p.alibi = alibi_slopes != nullptr;
   p.scale_log2 = scale * 1.4426950408889634f;

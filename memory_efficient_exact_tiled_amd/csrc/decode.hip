@@ -8,13 +8,19 @@
 // goal is to keep enough loads in flight and to read each K/V row once for
 // all query heads that share it.
 //
-// decode_split: one wave per (sequence b, KV head g, block of up to 16 of g's
-//   query heads, chunk of kDecodeChunk keys); the 8 waves of a work-group take
-//   8 consecutive (g, block) units of the same chunk, so they read the same
-//   cache rows (all KV heads of a position sit side by side) at the same
-//   time. Chunks at or past ctx exit at once. A wave walks its chunk 16 keys
-//   per step with two register stages (the next step's loads are in flight
-//   while the current one is computed):
+// decode_plan: prefix sums of the context lengths and the span L of keys per
+//   split work-group, L = max(kDecodeChunk, ceil(sum ctx / G)) for G split
+//   work-groups (one per compute unit), into the workspace header. Every
+//   split work-group then gets the same amount of work whatever the length
+//   mix, so no last round of long chunks runs on a mostly idle GPU.
+// decode_split: work-group w takes the keys [w L, (w+1) L) of the sequences
+//   laid end to end, for 8 consecutive (KV head g, block of up to 16 of g's
+//   query heads) units, one per wave: the 8 waves read the same cache rows
+//   (all KV heads of a position sit side by side) at the same time. A range
+//   that spans several sequences yields one partial per sequence, in slot
+//   w - floor(prefix[b] / L) of that sequence. A wave walks its keys 16 per
+//   step with two register stages (the next step's loads are in flight while
+//   the current one is computed):
 //     * K rows are loaded from HBM straight into the A-operand layout of
 //       v_mfma_f32_16x16x32 (row = key, k = head dim), the query heads of the
 //       group form the B operand (one column per head), so S^T = K Q^T reads
@@ -28,8 +34,8 @@
 //       whatever the cache holds there (NaN included) cannot reach the result.
 //   Each wave writes its partial (row max m in log2 units, row sum l,
 //   unnormalised O) per head to the workspace.
-// decode_combine: per (b, query head) merges the partials of all chunks by
-//   their maxima: O = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c, which
+// decode_combine: per (b, query head) merges the partials of the work-groups
+//   that covered the sequence by their maxima: O = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c, which
 //   is the block update of the online softmax ("FlashAttention (2022)",
 //   paithon.it, section on the softmax that needs not see the whole row).
 #include "common.hpp"
@@ -73,16 +79,30 @@ decode_split_kernel(const DecParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int chunk = blockIdx.x;
   const int unit = blockIdx.y * kWaves + wave;
-  const int b = blockIdx.z;
   if (unit >= p.Hkv * p.nhb) return;
   const int g = unit / p.nhb;
   const int hb = unit - g * p.nhb;
-  const int ctx = min(max(p.ctx[b], 0), p.S_max);
-  const int w0 = chunk * kDecodeChunk;
-  if (w0 >= ctx) return;
-  const int w1 = min(w0 + kDecodeChunk, ctx);
+  const int* prefix = p.plan;              // [B + 1] prefix sums of ctx, then L
+  const int total = prefix[p.B];
+  const int L = prefix[p.B + 1];
+  const long long lo64 = (long long)blockIdx.x * L;
+  if (lo64 >= total) return;
+  const int lo = (int)lo64;
+  const int hi = (int)min(lo64 + L, (long long)total);
+  // First sequence with keys at or past lo: the last b with prefix[b] <= lo
+  // whose prefix grows after it (binary search over the prefix sums).
+  int bl = 0, bh = p.B - 1;
+  while (bl < bh) {
+    const int mid = (bl + bh + 1) >> 1;
+    if (prefix[mid] <= lo) bl = mid; else bh = mid - 1;
+  }
+  for (int b = bl; b < p.B && prefix[b] < hi; ++b) {
+  const int ctx = prefix[b + 1] - prefix[b];
+  const int w0 = max(lo - prefix[b], 0);
+  const int w1 = min(hi - prefix[b], ctx);
+  if (w1 <= w0) continue;
+  const int slot = (int)(blockIdx.x - prefix[b] / L);
 
   const int col = lane & 15;     // query head within the block (MFMA column)
   const int grp = lane >> 4;
@@ -267,14 +287,44 @@ decode_split_kernel(const DecParams p) {
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (real) {
-    const long long slot = ((long long)b * p.Hq + h) * p.nchunk + chunk;
-    float* dst = p.ws_o + slot * D + grp * 4;
+    const long long ws = ((long long)b * p.Hq + h) * p.nsplit + slot;
+    float* dst = p.ws_o + ws * D + grp * 4;
 #pragma unroll
     for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16) = o[db];
     if (grp == 0) {
-      p.ws_ml[slot * 2 + 0] = m_run;
-      p.ws_ml[slot * 2 + 1] = l_tot;
+      p.ws_ml[ws * 2 + 0] = m_run;
+      p.ws_ml[ws * 2 + 1] = l_tot;
     }
+  }
+  }   // sequences of the range
+}
+
+// One work-group of 256 threads: inclusive prefix sums of the clamped context
+// lengths (256 at a time, with an LDS scan), then the span L.
+__global__ void __launch_bounds__(256) decode_plan_kernel(const DecParams p) {
+  __shared__ int sc[256];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  if (tid == 0) p.plan[0] = 0;
+  for (int base = 0; base < p.B; base += 256) {
+    const int i = base + tid;
+    int x = i < p.B ? min(max(p.ctx[i], 0), p.S_max) : 0;
+    sc[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int y = tid >= off ? sc[tid - off] : 0;
+      __syncthreads();
+      sc[tid] += y;
+      __syncthreads();
+    }
+    if (i < p.B) p.plan[i + 1] = carry + sc[tid];
+    carry += sc[255];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const long long per = ((long long)carry + p.grid - 1) / p.grid;
+    const long long L = max((long long)kDecodeChunk, (per + 15) / 16 * 16);
+    p.plan[p.B + 1] = (int)min(L, (long long)0x7fffffff);
   }
 }
 
@@ -292,9 +342,12 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int ctx = min(max(p.ctx[b], 0), p.S_max);
-  const int n = (ctx + kDecodeChunk - 1) / kDecodeChunk;
-  const long long base = ((long long)b * p.Hq + h) * p.nchunk;
+  const int* prefix = p.plan;
+  const int L = prefix[p.B + 1];
+  const int ctx = prefix[b + 1] - prefix[b];
+  // Partials of the work-groups floor(prefix[b] / L) .. floor((prefix[b] + ctx - 1) / L).
+  const int n = ctx > 0 ? (prefix[b] + ctx - 1) / L - prefix[b] / L + 1 : 0;
+  const long long base = ((long long)b * p.Hq + h) * p.nsplit;
 
   float m = -INFINITY;
   for (int i = tid; i < n; i += NT) m = fmaxf(m, p.ws_ml[(base + i) * 2]);
@@ -338,9 +391,12 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) 
 template <typename T, int D>
 hipError_t launch_typed(const DecParams& p, hipStream_t stream) {
   const int units = p.Hkv * p.nhb;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages>),
-                     dim3(p.nchunk, (units + kWaves - 1) / kWaves, p.B), dim3(kWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages>), dim3(p.grid, (units + kWaves - 1) / kWaves),
+                     dim3(kWaves * 64), 0, stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq, p.B), dim3(256), 0, stream, p);
   return hipGetLastError();

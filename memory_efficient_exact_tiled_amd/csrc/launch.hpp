@@ -37,9 +37,11 @@ struct DecParams {
   const int32_t* ctx;
   uint16_t* out;
   const float* slopes;
-  float* ws_o;           // [B][Hq][nchunk][D] unnormalised partial outputs
-  float* ws_ml;          // [B][Hq][nchunk][2] partial (row max in log2 units, row sum)
-  int B, Hq, Hkv, group, S_max, nchunk, nhb;
+  int* plan;             // [B + 2]: prefix sums of the clamped ctx, then the span L
+  float* ws_o;           // [B][Hq][nsplit][D] unnormalised partial outputs
+  float* ws_ml;          // [B][Hq][nsplit][2] partial (row max in log2 units, row sum)
+  int B, Hq, Hkv, group, S_max, nsplit, nhb;
+  int grid;              // split work-groups along x (one per compute unit)
   int alibi;
   float scale_log2;
 };

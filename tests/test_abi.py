@@ -39,9 +39,13 @@ def test_strerror_and_supported():
 def test_workspace_bytes():
     C = mea.decode_chunk()
     assert C == 512
-    nch = (32768 + C - 1) // C
-    o = 32 * 32 * nch * 128 * 4
-    assert mea.decode_workspace_bytes(32, 32, 128, 32768) == ((o + 255) // 256) * 256 + 32 * 32 * nch * 2 * 4
+    # plan header [B + 2] int32, then partials [B][Hq][nsplit][D] and their
+    # (max, sum) pairs, each part 256-byte aligned; a sequence is covered by
+    # at most ceil(S_max / C) + 1 spans of at least C keys
+    nsplit = (32768 + C - 1) // C + 1
+    o = 32 * 32 * nsplit * 128 * 4
+    head = ((32 + 2) * 4 + 255) // 256 * 256
+    assert mea.decode_workspace_bytes(32, 32, 128, 32768) == head + ((o + 255) // 256) * 256 + 32 * 32 * nsplit * 2 * 4
     assert mea.decode_workspace_bytes(0, 32, 128, 32768) == 0
 
 
@@ -94,6 +98,7 @@ def _dec(**kw):
     (dict(Hq=6, Hkv=4), mea.MEA_EINVAL),
     (dict(scale=-1.0), mea.MEA_EINVAL),
     (dict(D=32), mea.MEA_EUNSUPPORTED),
+    (dict(B=4, S=1 << 29), mea.MEA_EINVAL),    # context prefix sums overflow int32
     (dict(ws=None), mea.MEA_EWORKSPACE),
     (dict(wsb=16), mea.MEA_EWORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100010)), mea.MEA_EWORKSPACE),

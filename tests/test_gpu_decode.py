@@ -25,6 +25,12 @@ SMALL = [
     ("empty_context", 3, [0, 5, 0], 64, 4, 1, 128, "bf16", False),
     ("group_20_two_head_blocks", 4, [700, 33], 800, 40, 2, 64, "bf16", True),
     ("mha_group_1", 5, [900, 1], 1000, 6, 6, 128, "fp16", False),
+    # many short sequences (some empty) share one split work-group's span
+    ("many_short_in_one_span", 6, [int(x) for x in np.random.default_rng(6).integers(0, 100, 40)] + [3000],
+     3000, 8, 2, 64, "bf16", True),
+    # more keys than 512 per compute unit: spans longer than the chunk,
+    # crossing sequence boundaries mid-span
+    ("long_spans", 7, [70000, 70001, 1, 9000], 70001, 4, 1, 64, "fp16", True),
 ]
 
 
