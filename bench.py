@@ -401,8 +401,9 @@ def main():
         "roofline_decode": None if dec_gbs is None else {
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic_for(traffic, "decode_split_kernelIDF16bLi128", "decode_combine_kernelIDF16bLi128"),
-            "kernel": "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
+            "traffic": traffic_for(traffic, "decode_plan_kernel", "decode_split_kernelIDF16bLi128",
+                                   "decode_combine_kernelIDF16bLi128"),
+            "kernel": "decode_plan_kernel + decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
             "avg_launch_us": round(ms["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes,
         },
         "roofline_bwd": None if "bwd_noncausal" not in tflops else {

@@ -31,7 +31,9 @@
 //       O^T = V^T P^T (v_mfma_f32_16x16x16);
 //     * all K/V loads are buffer loads whose resource ends at the chunk's
 //       last key: slots at or past ctx read as zeros and are masked, so
-//       whatever the cache holds there (NaN included) cannot reach the result.
+//       whatever the cache holds there (NaN included) cannot reach the result;
+//       they use the non-temporal cache policy, since each cache row is read
+//       once per step;
 //   Each wave writes its partial (row max m in log2 units, row sum l,
 //   unnormalised O) per head to the workspace.
 // decode_combine: per (b, query head) merges the partials of the work-groups
@@ -158,9 +160,9 @@ decode_split_kernel(const DecParams p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int st = 0; st < DS; ++st)
-        sg.kf[kb][st] = __builtin_bit_cast(v8, buf_load16(rk, koff_lane + kb * 16 * row_bytes + st * 64));
+        sg.kf[kb][st] = __builtin_bit_cast(v8, buf_load16_nt(rk, koff_lane + kb * 16 * row_bytes + st * 64));
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) sg.vst[i] = buf_load16(rv, voff_lane[i]);
+    for (int i = 0; i < NLD; ++i) sg.vst[i] = buf_load16_nt(rv, voff_lane[i]);
   };
   auto compute = [&](const Stage& sg, int key0) {
     f32x4 s[KB];
