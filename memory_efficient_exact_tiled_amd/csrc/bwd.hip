@@ -71,7 +71,11 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
 }
 
 // ---- Delta and lse in log2 units --------------------------------------------
-// D/8 lanes per (row, head): each loads 16 bytes of O and dO.
+// D/8 lanes per (row, head): each loads 16 bytes of O and dO. Items run in
+// the lse layout ([batch][head][query], query fastest), so the lse reads and
+// the Delta / lse2 writes of a wave are contiguous (the (row, head) order
+// fetched twice the algorithmic bytes through those scattered 4-byte
+// accesses).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
   constexpr int CPR = D / 8;
@@ -80,19 +84,18 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
   const long long n_items = p.rows * p.Hq;
   for (long long item = (long long)blockIdx.x * IPB + threadIdx.x / CPR; item < n_items;
        item += (long long)gridDim.x * IPB) {
-    const long long row = item / p.Hq;
-    const int h = (int)(item - row * p.Hq);
-    const long long e = row * p.q_rstride + (long long)h * D + sub * 8;
+    const long long bh = item / p.M;
+    const long long i = item - bh * p.M;
+    const long long b = bh / p.Hq;
+    const int h = (int)(bh - b * p.Hq);
+    const long long e = (b * p.M + i) * p.q_rstride + (long long)h * D + sub * 8;
     float acc = dot8<T>(*reinterpret_cast<const uint4*>(p.out + e), *reinterpret_cast<const uint4*>(p.dout + e));
 #pragma unroll
     for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) {
-      const long long b = row / p.M;
-      const long long i = row - b * p.M;
-      const long long idx = (b * p.Hq + h) * p.M + i;
-      const float l = p.lse[idx];
-      p.delta[idx] = acc;
-      p.lse2[idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      const float l = p.lse[item];
+      p.delta[item] = acc;
+      p.lse2[item] = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
   }
 }
