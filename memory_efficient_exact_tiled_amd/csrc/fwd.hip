@@ -525,15 +525,21 @@ hipError_t launch_k(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Launch shapes (fwd_block_m must agree): the dense launch runs QB=2 at D=64;
-// causal and block-sparse launches run QB=1 (128-row work-groups), which
-// halves the rows a diagonal block masks off and keeps the skip list of a
-// work-group close to what each wave needs.
+// Launch shapes (fwd_block_m must agree): the dense D=64 launch runs QB=2
+// (256-row work-groups) when that still gives every compute unit two
+// work-groups (p.wide, set by the host), else QB=1; causal and block-sparse
+// launches run QB=1 (128-row work-groups), which halves the rows a diagonal
+// block masks off and keeps the skip list of a work-group close to what each
+// wave needs.
 template <typename T, int D>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int kDenseQB = D == 64 ? 2 : 1;
   if (p.block_mask != nullptr) return launch_k<T, D, 1, 2, 2, 1>(p, stream);
-  if (!p.causal) return launch_k<T, D, kDenseQB, 2, 2, 0>(p, stream);
+  if (!p.causal) {
+    if constexpr (D == 64) {
+      if (p.wide) return launch_k<T, D, 2, 2, 2, 0>(p, stream);
+    }
+    return launch_k<T, D, 1, 2, 2, 0>(p, stream);
+  }
   return p.alibi ? launch_k<T, D, 1, 1, 1, 0>(p, stream) : launch_k<T, D, 1, 1, 0, 0>(p, stream);
 }
 
@@ -544,8 +550,8 @@ hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int fwd_block_m(int D, bool causal, bool block_sparse) {
-  if (D == 64) return (causal || block_sparse) ? FwdShape<64, 1>::BM : FwdShape<64, 2>::BM;
+int fwd_block_m(int D, bool causal, bool block_sparse, bool wide) {
+  if (D == 64) return (wide && !causal && !block_sparse) ? FwdShape<64, 2>::BM : FwdShape<64, 1>::BM;
   return FwdShape<128, 1>::BM;
 }
 

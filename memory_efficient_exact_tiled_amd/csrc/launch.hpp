@@ -20,6 +20,7 @@ struct FwdParams {
   int nkb;                 // key blocks per mask row: ceil(N/64)
   int B, M, N, Hq, Hkv, group;
   int causal, varlen, alibi;
+  int wide;              // dense D=64 without mask: 256-row work-groups (else 128)
   float scale_log2;      // scale * log2(e)
   int n_qtiles;          // dense: q tiles per (batch, head); packed: bound on tiles over all segments
   int total_wg;          // logical work-groups
@@ -76,8 +77,9 @@ struct BwdParams {
   int kv_rstride;
 };
 
-// Query rows per forward work-group and the decode chunk length.
-int fwd_block_m(int D, bool causal, bool block_sparse);
+// Query rows per forward work-group (wide: the 256-row dense D=64 tiles) and
+// the decode chunk length.
+int fwd_block_m(int D, bool causal, bool block_sparse, bool wide);
 constexpr int kSparseBlock = 64;   // block edge of block-sparse masks
 constexpr int kDecodeChunk = 512;
 

@@ -28,6 +28,10 @@ SMALL = [
     # many short sequences (some empty) share one split work-group's span
     ("many_short_in_one_span", 6, [int(x) for x in np.random.default_rng(6).integers(0, 100, 40)] + [3000],
      3000, 8, 2, 64, "bf16", True),
+    # more than 256 sequences: the context prefix sums carry across the
+    # plan's 256-wide scan steps
+    ("batch_300_scan_carry", 8, [int(x) for x in np.random.default_rng(8).integers(0, 60, 300)], 64, 2, 1, 64,
+     "fp16", False),
     # more keys than 512 per compute unit: spans longer than the chunk,
     # crossing sequence boundaries mid-span
     ("long_spans", 7, [70000, 70001, 1, 9000], 70001, 4, 1, 64, "fp16", True),

@@ -83,6 +83,24 @@ def test_seqlen_sweep_sampled(mea, M, causal):
         assert report(f"{name} b{b}", got[b, rows], want, TOL["bf16"]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dt,alibi", [("bf16", False), ("fp16", True)])
+def test_dense_wide_tiles_ragged(mea, dt, alibi):
+    """Dense D=64 without mask at a size that takes the 256-row work-groups
+    (B*Hq*ceil(M/256) >= 512), with M and N off the tile grid and M != N;
+    sampled rows at the tile edges against the oracle."""
+    B, M, N, Hq, Hkv = 8, 1000, 1100, 16, 4
+    name = f"wide_{dt}{'_alibi' if alibi else ''}"
+    say(f"case {name}")
+    c = inp.dense_case(77, B, M, N, Hq, Hkv, 64, dt)
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    out, _, scale = _run(mea, c, dt, slopes=slopes)
+    got = host_f64(out)
+    rows = np.array([0, 1, 31, 32, 63, 64, 255, 256, 511, 512, 767, 768, 998, 999])
+    for b in (0, 7):
+        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], dt, scale, b, rows, alibi_slopes=slopes)
+        assert report(f"{name} b{b}", got[b, rows], want, TOL[dt]) <= TOL[dt]
+
+
 def test_varlen_gqa_alibi_full_config(mea):
     """8 packed segments, lengths uniform in [64, 2048] (seeded), Hq=32, Hkv=8,
     D=128, bf16, block-diagonal causal + ALiBi: sampled rows of every segment."""
