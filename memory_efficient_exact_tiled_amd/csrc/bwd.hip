@@ -137,11 +137,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
+  // Launch order as in the forward: dense causal launches issue the tiles
+  // longest first over all (batch, head) pairs, round-robin over the XCDs;
+  // the others give each XCD a contiguous range of (batch, head, tile).
   const int pid = blockIdx.x;
-  const int lid = (pid & 7) * p.wg_per_xcd_q + (pid >> 3);
-  if (lid >= p.total_wg_q) return;
-  const int bh = lid / p.n_qtiles;
-  const int t = lid - bh * p.n_qtiles;
+  int bh, t;
+  if (CS == 1 && !p.varlen) {
+    if (pid >= p.total_wg_q) return;
+    const int nbh = p.B * p.Hq;
+    t = pid / nbh;
+    bh = pid - t * nbh;
+  } else {
+    const int lid = (pid & 7) * p.wg_per_xcd_q + (pid >> 3);
+    if (lid >= p.total_wg_q) return;
+    bh = lid / p.n_qtiles;
+    t = lid - bh * p.n_qtiles;
+  }
   const int h = bh % p.Hq;
   const int b = bh / p.Hq;
   const int g = h / p.group;
@@ -367,11 +378,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
+  // Under a causal mask key tile 0 sees the most queries: dense causal
+  // launches issue tile ranks in order over all (batch, KV head) pairs,
+  // round-robin over the XCDs, as the dQ kernel does.
   const int pid = blockIdx.x;
-  const int lid = (pid & 7) * p.wg_per_xcd_k + (pid >> 3);
-  if (lid >= p.total_wg_k) return;
-  const int bg = lid / p.n_ktiles;
-  const int t = lid - bg * p.n_ktiles;
+  int bg, t;
+  if (CS == 1 && !p.varlen) {
+    if (pid >= p.total_wg_k) return;
+    const int nbg = p.B * p.Hkv;
+    t = pid / nbg;
+    bg = pid - t * nbg;
+  } else {
+    const int lid = (pid & 7) * p.wg_per_xcd_k + (pid >> 3);
+    if (lid >= p.total_wg_k) return;
+    bg = lid / p.n_ktiles;
+    t = lid - bg * p.n_ktiles;
+  }
   const int g = bg % p.Hkv;
   const int b = bg / p.Hkv;
 
