@@ -137,14 +137,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Launch order as in the forward: dense causal launches issue the tiles
-  // longest first over all (batch, head) pairs, round-robin over the XCDs;
-  // the others give each XCD a contiguous range of (batch, head, tile).
+  // Launch order as in the forward: causal launches are tile index major
+  // with the heads innermost, round-robin over the XCDs (dense: longest tiles
+  // first over all (batch, head) pairs; packed: segment by segment); the
+  // others give each XCD a contiguous range of (batch, head, tile).
   const int pid = blockIdx.x;
   int bh, t;
-  if (CS == 1 && !p.varlen) {
+  if (CS == 1) {
     if (pid >= p.total_wg_q) return;
-    const int nbh = p.B * p.Hq;
+    const int nbh = p.varlen ? p.Hq : p.B * p.Hq;
     t = pid / nbh;
     bh = pid - t * nbh;
   } else {
@@ -378,14 +379,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Under a causal mask key tile 0 sees the most queries: dense causal
-  // launches issue tile ranks in order over all (batch, KV head) pairs,
-  // round-robin over the XCDs, as the dQ kernel does.
+  // Under a causal mask key tile 0 sees the most queries: causal launches
+  // are tile index major with the KV heads innermost, round-robin over the
+  // XCDs, as in the dQ kernel.
   const int pid = blockIdx.x;
   int bg, t;
-  if (CS == 1 && !p.varlen) {
+  if (CS == 1) {
     if (pid >= p.total_wg_k) return;
-    const int nbg = p.B * p.Hkv;
+    const int nbg = p.varlen ? p.Hkv : p.B * p.Hkv;
     t = pid / nbg;
     bg = pid - t * nbg;
   } else {

@@ -51,11 +51,14 @@
 // Launch order: work-group p runs on XCD p % 8. Without a causal mask each
 // XCD is given a contiguous range of logical work-groups, so the query tiles
 // of one head (which read the same K/V) share that XCD's L2. Under a causal
-// mask the tiles differ in length by up to the sequence length: dense
-// launches issue the tiles longest first over all (batch, head) pairs, dealt
-// round-robin over the XCDs (measured 13-31 % faster at M = 1024..4096 than
-// per-head order with XCD ranges); packed launches issue each segment's
-// tiles longest first.
+// mask the tiles differ in length by up to the sequence length, and the
+// launch is tile index major with the heads innermost, dealt round-robin
+// over the XCDs: dense launches issue every (batch, head)'s longest tile
+// before any second-longest one (measured 13-31 % faster at M = 1024..4096
+// than per-head order with XCD ranges); packed launches go segment by
+// segment, each segment's tiles longest first (+5-8 % on 8 segments of
+// 64..2048 tokens; a strict longest-first order over all segments measured
+// slower).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -120,12 +123,13 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   // ---- work decomposition -------------------------------------------------
   const int pid = blockIdx.x;
   int bh, t;
-  if (CS == 1 && !p.varlen) {
-    // Dense causal: tile rank major, so every (batch, head)'s longest tile
-    // is issued before any second-longest one, dealt round-robin over the
-    // XCDs.
+  if (CS == 1) {
+    // Causal: tile index major, heads innermost, dealt round-robin over the
+    // XCDs. Dense: every (batch, head)'s longest tile is issued before any
+    // second-longest one. Packed: segment by segment, each segment's tiles
+    // longest first, for all heads at once.
     if (pid >= p.total_wg) return;
-    const int nbh = p.B * p.Hq;
+    const int nbh = p.varlen ? p.Hq : p.B * p.Hq;
     t = pid / nbh;
     bh = pid - t * nbh;
   } else {
