@@ -23,6 +23,11 @@ time, measured with HIP events on the stream the kernel runs on); the other
 items are reported beside it, decode as algorithmic HBM GB/s (K and V bytes
 of every sequence's context plus q and out). Progress goes to stderr.
 
+The roofline objects of items 1 and 4 also carry ``alone``: the same kernel
+timed over ALONE consecutive launches on its own (its sustained throughput
+outside the mixed step). Runs need tens of milliseconds of warmup before the
+GPU clock settles; --warmup steps provide it.
+
 ``cpu_baseline`` times the fp64 oracle (test infrastructure) on the host's
 cores over a bounded sample of item 1 (rows of the first batch row, all
 heads, until about --cpu-seconds have passed); ``cpu_baseline_decode`` does
@@ -44,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ALONE = 100                   # back-to-back launches of the headline items timed on their own
 
 
 def log(*a):
@@ -341,6 +347,22 @@ def main():
     log(f"[bench] timed {args.steps} steps in {wall:.3f}s")
 
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev])) for n, ev in events.items()}
+
+    # The headline forward and the decode are also timed on their own, outside
+    # the mixed step: ALONE launches in a row between two events.
+    alone = {}
+    for name, fn in items:
+        if name not in ("fwd_noncausal", "decode"):
+            continue
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(ALONE):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        alone[name] = e0.elapsed_time(e1) / ALONE
     L = x["lengths"].astype(np.int64)
     flops_all = {
         "fwd_noncausal": 4.0 * 4 * 16 * 4096 * 4096 * 64,
@@ -365,6 +387,12 @@ def main():
             log(f"[bench] decode: {ms[n] * 1e3:.1f} us  {dec_gbs:.1f} GB/s ({dec_gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
             per_item[n] = {"avg_launch_us": round(ms[n] * 1e3, 2), "gbs": round(dec_gbs, 1),
                            "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dec_bytes}
+    for n, t in alone.items():
+        if n in tflops:
+            log(f"[bench] {n} alone ({ALONE} back to back): {t * 1e3:.1f} us  "
+                f"{flops_all[n] / (t * 1e-3) / 1e12:.1f} TFLOP/s")
+        else:
+            log(f"[bench] {n} alone ({ALONE} back to back): {t * 1e3:.1f} us  {dec_bytes / (t * 1e-3) / 1e9:.1f} GB/s")
     head = tflops.get("fwd_noncausal")
     traffic = measured_traffic()
 
@@ -397,6 +425,11 @@ def main():
             "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
             "kernel": "fwd_kernel<bf16,64,QB=2>", "avg_launch_us": round(ms["fwd_noncausal"] * 1e3, 2),
             "algorithmic_flops": flops_all["fwd_noncausal"],
+            "alone": None if "fwd_noncausal" not in alone else {
+                "launches_back_to_back": ALONE, "avg_launch_us": round(alone["fwd_noncausal"] * 1e3, 2),
+                "achieved": round(flops_all["fwd_noncausal"] / (alone["fwd_noncausal"] * 1e-3) / 1e12, 2),
+                "frac": round(flops_all["fwd_noncausal"] / (alone["fwd_noncausal"] * 1e-3) / 1e12
+                              / PEAK_MFMA_TFLOPS, 4)},
         },
         "roofline_decode": None if dec_gbs is None else {
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -405,6 +438,10 @@ def main():
                                    "decode_combine_kernelIDF16bLi128"),
             "kernel": "decode_plan_kernel + decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
             "avg_launch_us": round(ms["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes,
+            "alone": None if "decode" not in alone else {
+                "launches_back_to_back": ALONE, "avg_launch_us": round(alone["decode"] * 1e3, 2),
+                "achieved": round(dec_bytes / (alone["decode"] * 1e-3) / 1e9, 1),
+                "frac": round(dec_bytes / (alone["decode"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         },
         "roofline_bwd": None if "bwd_noncausal" not in tflops else {
             "bound": "mfma", "achieved": round(tflops["bwd_noncausal"], 2), "peak": PEAK_MFMA_TFLOPS,
