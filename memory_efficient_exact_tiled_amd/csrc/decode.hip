@@ -29,8 +29,8 @@
 //     * V rows go HBM -> registers -> the wave's LDS region and come back
 //       transposed through ds_read_b64_tr_b16 as the A operand of
 //       O^T = V^T P^T (v_mfma_f32_16x16x16);
-//     * all K/V loads are buffer loads whose resource ends at the chunk's
-//       last key: slots at or past ctx read as zeros and are masked, so
+//     * all K/V loads are buffer loads whose resource ends at the last key
+//       of the sequence's part of the span: slots at or past ctx read as zeros and are masked, so
 //       whatever the cache holds there (NaN included) cannot reach the result;
 //       they use the non-temporal cache policy, since each cache row is read
 //       once per step;
@@ -59,9 +59,9 @@ struct DecShape {
   static constexpr int NLD = KSTEP * CPR / 64;     // V chunks per lane per step
 };
 
-// One wave = one (KV head g, block of up to 16 of g's query heads) over one
-// chunk of keys; the waves of a work-group take consecutive units, so they
-// read the same cache rows at the same time. KSTEP keys per step (16 or 32);
+// One wave = one (KV head g, block of up to 16 of g's query heads) over the
+// work-group's span of keys; the waves of a work-group take consecutive
+// units, so they read the same cache rows at the same time. KSTEP keys per step (16 or 32);
 // STAGES register stages of K/V: the loads of the next STAGES-1 steps are in
 // flight while the current step is computed.
 template <typename T, int D, int KSTEP, int STAGES>
@@ -141,8 +141,8 @@ decode_split_kernel(const DecParams p) {
     uint4 vst[NLD];   // V rows, bound for LDS
   };
   // Per-lane byte offsets inside one step's rows; the buffer resource is
-  // rebased on each step and ends at the chunk's last key, so rows past it
-  // read as zeros.
+  // rebased on each step and ends at the last key of this sequence's part of
+  // the span, so rows past it read as zeros.
   const uint32_t row_bytes = (uint32_t)rstride * 2u;
   const uint32_t koff_lane = (uint32_t)col * row_bytes + (uint32_t)grp * 16u;
   uint32_t voff_lane[NLD];
@@ -174,7 +174,7 @@ decode_split_kernel(const DecParams p) {
       for (int st = 0; st < DS; ++st) s[kb] = MF::mma16(sg.kf[kb][st], qf[st], s[kb]);
     }
 
-    // Scores in log2 units; keys past the chunk are masked.
+    // Scores in log2 units; keys past the sequence's part of the span are masked.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -285,7 +285,7 @@ decode_split_kernel(const DecParams p) {
     }
   }
 
-  // ---- this wave's partial for the chunk ------------------------------------
+  // ---- this wave's partial for the sequence's part of the span -----------------
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (real) {
@@ -331,8 +331,8 @@ __global__ void __launch_bounds__(256) decode_plan_kernel(const DecParams p) {
 }
 
 // One work-group of 256 threads per (sequence, query head). Thread t reads
-// column d = t % D of the partial outputs of chunks c = t / D, t / D + 256 / D,
-// ... so every chunk's row is one coalesced read, and the 256 / D column
+// column d = t % D of the partial outputs of slots c = t / D, t / D + 256 / D,
+// ... so every slot's row is one coalesced read, and the 256 / D column
 // groups are summed through LDS at the end.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) {

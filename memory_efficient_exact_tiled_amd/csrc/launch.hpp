@@ -78,7 +78,7 @@ struct BwdParams {
 };
 
 // Query rows per forward work-group (wide: the 256-row dense D=64 tiles) and
-// the decode chunk length.
+// the shortest span of keys of a decode split work-group.
 int fwd_block_m(int D, bool causal, bool block_sparse, bool wide);
 constexpr int kSparseBlock = 64;   // block edge of block-sparse masks
 constexpr int kDecodeChunk = 512;
