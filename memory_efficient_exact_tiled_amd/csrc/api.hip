@@ -114,12 +114,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
   const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
   if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
   if (block_mask != nullptr && (varlen || kv_lens != nullptr)) return MEA_EINVAL;
-  // Dense D=64 without mask takes 256-row work-groups when there are enough
-  // of them for two per compute unit; otherwise 128-row ones keep the GPU
-  // full (measured +14 to +37 % at M <= 1024, B=4, H=16).
   // Work-group counts are int32; checked here at the smallest tile height.
   const long long t128 = varlen ? ((long long)M + 127) / 128 + B : ((long long)M + 127) / 128 * B;
   if (t128 * Hq > 0x7fffffffLL - 8) return MEA_EINVAL;
+  // Dense D=64 without mask takes 256-row work-groups when there are enough
+  // of them for two per compute unit; otherwise 128-row ones keep the GPU
+  // full (measured +13 to +39 % at M <= 1024, B=4, H=16).
   bool wide = false;
   if (D == 64 && !causal && block_mask == nullptr) {
     const long long t256 = varlen ? ((long long)M + 255) / 256 + B : ((long long)M + 255) / 256 * B;
