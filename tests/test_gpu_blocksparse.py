@@ -39,6 +39,8 @@ CASES = [
     ("causal_alibi_m333_d128_fp16", 1, 1, 333, 333, 4, 4, 128, "fp16", True, True, 0.5),
     ("causal_m512_d64_bf16_sparse", 2, 2, 512, 512, 8, 2, 64, "bf16", True, False, 0.25),
     ("noncausal_alibi_m200_n700_d128_bf16", 3, 1, 200, 700, 2, 1, 128, "bf16", False, True, 0.3),
+    # 300 key blocks: the skip list moves to its second 256-block window
+    ("causal_alibi_two_windows_m128_n19200_d64_bf16", 5, 1, 128, 19200, 2, 1, 64, "bf16", True, True, 0.3),
 ]
 
 
@@ -61,16 +63,18 @@ def test_blocksparse_parity(mea, case):
     assert np.all(host_f64(out)[:, (bm.shape[0] - 1) * 64:] == 0), "query block with every block off"
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
-def test_all_on_mask_is_the_dense_kernel_bitwise(mea, D):
+def test_all_on_mask_is_the_dense_kernel_bitwise(mea, D, causal):
     """With every block on, the skip list visits every key block in order:
-    the same arithmetic as the dense forward."""
-    say(f"case blocksparse all-on D={D}")
+    the same arithmetic as the dense forward (no ALiBi: the dense causal
+    ALiBi launch walks the blocks in reverse)."""
+    say(f"case blocksparse all-on D={D} causal={causal}")
     c = inp.dense_case(4 + D, 2, 257, 300, 4, 2, D, "bf16")
     q, k, v = dev(c["q"], "bf16"), dev(c["k"], "bf16"), dev(c["v"], "bf16")
     ones = torch.ones((-(-257 // 64), -(-300 // 64)), dtype=torch.uint8, device="cuda")
-    a = mea.fwd(q, k, v)
-    b = mea.fwd_blocksparse(q, k, v, ones)
+    a = mea.fwd(q, k, v, causal=causal)
+    b = mea.fwd_blocksparse(q, k, v, ones, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
