@@ -6,9 +6,12 @@ import torch
 
 TOL = {"fp16": 2e-3, "bf16": 1.6e-2}   # max-abs error against the fp64 oracle (fp32 accumulation)
 # Row log-sum-exp: the normaliser l sums P after P is rounded to the input type
-# (the weights P.V really uses), so |dl/l| <= 2^-9 (bf16) or 2^-11 (fp16) and
-# |d lse| <= that bound; the margin covers fp32 accumulation and the final log.
-LSE_TOL = {"fp16": 2.0 ** -11 * 1.25, "bf16": 2.0 ** -9 * 1.25}
+# (the weights P.V really uses), so |dl/l| <= u, the unit roundoff of that type
+# (bf16: 8-bit significand, u = 2^-8; fp16: 11-bit, u = 2^-11), and
+# |d lse| <= ln(1 + u) < u. The bound is reached when a few weights dominate a
+# row and round the same way (a steep ALiBi slope); the margin covers fp32
+# accumulation and the final log.
+LSE_TOL = {"fp16": 2.0 ** -11 * 1.25, "bf16": 2.0 ** -8 * 1.25}
 TORCH_DTYPE = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
