@@ -10,9 +10,11 @@
 //
 // Work decomposition (one work-group = 4 waves = 256 threads):
 //   * a work-group owns BM = 4 * 32 * QB query rows of one (batch or packed
-//     segment, query head); wave w owns 32 * QB consecutive rows; two waves
-//     (three at QB=1, D=64) share each SIMD, so one wave's softmax overlaps
-//     another's matrix-core work; MFMA phases run at raised wave priority;
+//     segment, query head); wave w owns 32 * QB consecutive rows (QB = 2 for
+//     dense D=64 when that still gives two work-groups per compute unit,
+//     else 1); two waves (three at QB=1, D=64) share each SIMD, so one
+//     wave's softmax overlaps another's matrix-core work; MFMA phases run at
+//     raised wave priority;
 //   * K/V blocks of BN = 64 keys are copied to LDS with buffer loads whose
 //     resource ends at the segment's last key (rows past it read as zeros):
 //     straight into LDS (LDS DMA) at D=128, through registers at D=64 (the
@@ -28,9 +30,8 @@
 //     over those rounded values, two at a time with v_dot2_f32_{bf16,f16}
 //     (so the normaliser matches the weights P.V actually uses), and P^T is
 //     fed straight back as the B operand of O^T = V^T P^T; V^T comes from the
-//     row-major V block
-//     with ds_read_b64_tr_b16, which matches the key order P^T has in the
-//     score accumulators, so V is never transposed in memory;
+//     row-major V block with ds_read_b64_tr_b16, which matches the key order
+//     P^T has in the score accumulators, so V is never transposed in memory;
 //   * causal and block-diagonal masks are index predicates evaluated only on
 //     blocks that straddle the diagonal or the segment end; blocks entirely
 //     above the diagonal are never visited (per work-group) or computed (per
