@@ -301,31 +301,37 @@ decode_split_kernel(const DecParams p) {
   }   // sequences of the range
 }
 
-// One work-group of 256 threads: inclusive prefix sums of the clamped context
-// lengths (256 at a time, with an LDS scan), then the span L.
-__global__ void __launch_bounds__(256) decode_plan_kernel(const DecParams p) {
-  __shared__ int sc[256];
-  const int tid = threadIdx.x;
-  int carry = 0;
-  if (tid == 0) p.plan[0] = 0;
-  for (int base = 0; base < p.B; base += 256) {
-    const int i = base + tid;
-    int x = i < p.B ? min(max(p.ctx[i], 0), p.S_max) : 0;
-    sc[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int y = tid >= off ? sc[tid - off] : 0;
-      __syncthreads();
-      sc[tid] += y;
-      __syncthreads();
-    }
-    if (i < p.B) p.plan[i + 1] = carry + sc[tid];
-    carry += sc[255];
-    __syncthreads();
+// One wave: prefix sums of the clamped context lengths, then the span L.
+// Lane i takes sequences [i * per, (i + 1) * per): it sums them, a wave-wide
+// shuffle scan gives each lane its starting offset, and a second pass writes
+// the running sums (no LDS, no barrier).
+__global__ void __launch_bounds__(64) decode_plan_kernel(const DecParams p) {
+  const int lane = threadIdx.x;
+  const int per = (p.B + 63) / 64;
+  const int b0 = lane * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < p.B) sum += min(max(p.ctx[b], 0), p.S_max);
   }
-  if (tid == 0) {
-    const long long per = ((long long)carry + p.grid - 1) / p.grid;
-    const long long L = max((long long)kDecodeChunk, (per + 15) / 16 * 16);
+  int x = sum;   // inclusive scan over the lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  int run = x - sum;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < p.B) {
+      run += min(max(p.ctx[b], 0), p.S_max);
+      p.plan[b + 1] = run;
+    }
+  }
+  if (lane == 0) p.plan[0] = 0;
+  if (lane == 63) {
+    const long long per_wg = ((long long)x + p.grid - 1) / p.grid;   // x: the total at the last lane
+    const long long L = max((long long)kDecodeChunk, (per_wg + 15) / 16 * 16);
     p.plan[p.B + 1] = (int)min(L, (long long)0x7fffffff);
   }
 }
@@ -393,7 +399,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) 
 template <typename T, int D>
 hipError_t launch_typed(const DecParams& p, hipStream_t stream) {
   const int units = p.Hkv * p.nhb;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages>), dim3(p.grid, (units + kWaves - 1) / kWaves),
