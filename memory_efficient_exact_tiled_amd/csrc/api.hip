@@ -1,6 +1,7 @@
 // C ABI of libmea.so (declared in include/mea.h): host-side validation,
 // launch geometry, status codes. Validation happens before any HIP call, so
 // an invalid call touches neither the device nor the runtime.
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -22,16 +23,18 @@ bool dtype_ok(int dtype) { return dtype == MEA_FP16 || dtype == MEA_BF16; }
 
 // Compute units of the current device, queried once per device (256 if the
 // query fails). Called only after a call's arguments have been validated.
+// Calls from several host threads may race to fill an entry; they store the
+// same value, and the entries are atomics so that race is well defined.
 int device_compute_units() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 bool dim_ok(int D) { return D == 64 || D == 128; }
 
