@@ -231,7 +231,10 @@ int mea_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_n
  * workspace     device buffer of at least mea_decode_workspace_bytes(B, Hq, D,
  *               S_max) bytes, 256-byte aligned, owned by the caller; its
  *               contents on entry are ignored. Concurrent calls must not
- *               share a workspace.
+ *               share a workspace. Its size does not depend on S_max: the
+ *               partials take (1024 + B) * Hq * (D + 2) fp32 values (at most
+ *               1024 split work-groups, one row per (work-group, sequence)
+ *               pair), after a header of B + 2 int32.
  * Returns MEA_OK or an error status (nothing launched on error).
  */
 size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max);
@@ -247,8 +250,7 @@ const char* mea_strerror(int status);
  * of supported kernels answers in the tutorial's setup section). */
 int mea_supported(int dtype, int D);
 
-/* Shortest span of keys of one decode split work-group (the granularity of
- * the decode workspace). */
+/* Shortest span of keys of one decode split work-group. */
 int mea_decode_chunk(void);
 
 #ifdef __cplusplus

@@ -373,18 +373,20 @@ int mea_bwd_blocksparse(const void* q, const void* k, const void* v, const void*
 namespace {
 
 // Decode workspace: the plan ([B + 2] int32: prefix sums of ctx, then the span
-// of keys per split work-group), then the partial outputs [B][Hq][nsplit][D]
-// and (max, sum) pairs [B][Hq][nsplit][2], each part 256-byte aligned. A
-// sequence is covered by at most ceil(S_max / kDecodeChunk) + 1 work-groups.
+// of keys per split work-group), then the partial outputs [R][Hq][D] and the
+// (max, sum) pairs [R][Hq][2], R = kDecodeMaxSplit + B rows, each part
+// 256-byte aligned. Split work-group w writes its partial of sequence b to row
+// w + b: the sequences of a work-group are consecutive and so are the
+// work-groups of a sequence, so w + b is unique and below G + B for
+// G <= kDecodeMaxSplit work-groups, whatever S_max is.
 struct DecLayout {
   size_t plan, o, ml, total;
-  long long nsplit;
 };
 
-DecLayout dec_layout(int B, int Hq, int D, int S_max) {
+DecLayout dec_layout(int B, int Hq, int D) {
   DecLayout l{};
-  l.nsplit = ((long long)S_max + mea::kDecodeChunk - 1) / mea::kDecodeChunk + 1;
-  const size_t slots = (size_t)B * (size_t)Hq * (size_t)l.nsplit;
+  const size_t rows = (size_t)mea::kDecodeMaxSplit + (size_t)B;
+  const size_t slots = rows * (size_t)Hq;
   l.plan = ((size_t)(B + 2) * sizeof(int32_t) + 255) & ~(size_t)255;
   l.o = (slots * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
   l.ml = slots * 2 * sizeof(float);
@@ -398,7 +400,7 @@ extern "C" {
 
 size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {
   if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
-  return dec_layout(B, Hq, D, S_max).total;
+  return dec_layout(B, Hq, D).total;
 }
 
 int mea_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
@@ -416,10 +418,10 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   const size_t need = mea_decode_workspace_bytes(B, Hq, D, S_max);
   if (workspace == nullptr || workspace_bytes < need) return MEA_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return MEA_EWORKSPACE;
-  const DecLayout lay = dec_layout(B, Hq, D, S_max);
+  const DecLayout lay = dec_layout(B, Hq, D);
   const int group = Hq / Hkv;
   const int nhb = (group + 15) / 16;
-  if (lay.nsplit > 0x7fffffffLL || (long long)Hkv * nhb > 65535 || B > 65535) return MEA_EINVAL;
+  if ((long long)Hkv * nhb > 65535 || B > 65535) return MEA_EINVAL;
 
   mea::DecParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -432,8 +434,8 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   p.plan = reinterpret_cast<int*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + lay.plan);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.plan + lay.o);
-  p.nsplit = (int)lay.nsplit;
-  p.grid = device_compute_units();   // split work-groups: one per compute unit
+  // Split work-groups: one per compute unit (8 waves fill one).
+  p.grid = device_compute_units() < mea::kDecodeMaxSplit ? device_compute_units() : mea::kDecodeMaxSplit;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -12,13 +12,16 @@
 //   split work-group, L = max(kDecodeChunk, ceil(sum ctx / G)) for G split
 //   work-groups (one per compute unit), into the workspace header. Every
 //   split work-group then gets the same amount of work whatever the length
-//   mix, so no last round of long chunks runs on a mostly idle GPU.
+//   mix, so no last round of long chunks runs on a mostly idle GPU, and a
+//   short batch (one sequence of a few thousand keys) still spreads over the
+//   whole GPU.
 // decode_split: work-group w takes the keys [w L, (w+1) L) of the sequences
 //   laid end to end, for 8 consecutive (KV head g, block of up to 16 of g's
 //   query heads) units, one per wave: the 8 waves read the same cache rows
 //   (all KV heads of a position sit side by side) at the same time. A range
-//   that spans several sequences yields one partial per sequence, in slot
-//   w - floor(prefix[b] / L) of that sequence. A wave walks its keys 16 per
+//   that spans several sequences yields one partial per sequence, in
+//   workspace row w + b (unique: a work-group's sequences are consecutive,
+//   and so are a sequence's work-groups). A wave walks its keys 16 per
 //   step with two register stages (the next step's loads are in flight while
 //   the current one is computed):
 //     * K rows are loaded from HBM straight into the A-operand layout of
@@ -30,8 +33,9 @@
 //       transposed through ds_read_b64_tr_b16 as the A operand of
 //       O^T = V^T P^T (v_mfma_f32_16x16x16);
 //     * all K/V loads are buffer loads whose resource ends at the last key
-//       of the sequence's part of the span: slots at or past ctx read as zeros and are masked, so
-//       whatever the cache holds there (NaN included) cannot reach the result;
+//       of the sequence's part of the span: cache slots at or past ctx read
+//       as zeros and are masked, so whatever the cache holds there (NaN
+//       included) cannot reach the result;
 //       they use the non-temporal cache policy, since each cache row is read
 //       once per step;
 //   Each wave writes its partial (row max m in log2 units, row sum l,
@@ -104,7 +108,7 @@ decode_split_kernel(const DecParams p) {
   const int w0 = max(lo - prefix[b], 0);
   const int w1 = min(hi - prefix[b], ctx);
   if (w1 <= w0) continue;
-  const int slot = (int)(blockIdx.x - prefix[b] / L);
+  const long long prow = (long long)blockIdx.x + b;   // workspace row of this partial
 
   const int col = lane & 15;     // query head within the block (MFMA column)
   const int grp = lane >> 4;
@@ -289,7 +293,7 @@ decode_split_kernel(const DecParams p) {
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (real) {
-    const long long ws = ((long long)b * p.Hq + h) * p.nsplit + slot;
+    const long long ws = prow * p.Hq + h;
     float* dst = p.ws_o + ws * D + grp * 4;
 #pragma unroll
     for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16) = o[db];
@@ -336,14 +340,17 @@ __global__ void __launch_bounds__(64) decode_plan_kernel(const DecParams p) {
   }
 }
 
-// One work-group of 256 threads per (sequence, query head). Thread t reads
-// column d = t % D of the partial outputs of slots c = t / D, t / D + 256 / D,
-// ... so every slot's row is one coalesced read, and the 256 / D column
-// groups are summed through LDS at the end.
+// One work-group of 256 threads per (sequence, query head). A partial's
+// output row (D floats) is read by D / 4 threads, 16 bytes each, so a pass
+// merges 1024 / D partials at once: thread t takes the float4 t % (D / 4) of
+// partials t / (D / 4), t / (D / 4) + 1024 / D, ... (independent loads, no
+// chain through memory even for the hundreds of partials of one long
+// sequence), and the 1024 / D groups are summed through LDS at the end.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) {
-  constexpr int NT = 256, CG = NT / D;
-  __shared__ float red[NT];
+  constexpr int NT = 256, TPR = D / 4, RPP = NT / TPR;   // threads per row, rows per pass
+  __shared__ f32x4 red[NT];
+  __shared__ float lred[RPP];
   __shared__ float wmax[NT / 64];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -353,12 +360,14 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) 
   const int* prefix = p.plan;
   const int L = prefix[p.B + 1];
   const int ctx = prefix[b + 1] - prefix[b];
-  // Partials of the work-groups floor(prefix[b] / L) .. floor((prefix[b] + ctx - 1) / L).
-  const int n = ctx > 0 ? (prefix[b] + ctx - 1) / L - prefix[b] / L + 1 : 0;
-  const long long base = ((long long)b * p.Hq + h) * p.nsplit;
+  // Partials of the work-groups w = floor(prefix[b] / L) .. floor((prefix[b] +
+  // ctx - 1) / L), in workspace rows w + b.
+  const int w0 = prefix[b] / L;
+  const int n = ctx > 0 ? (prefix[b] + ctx - 1) / L - w0 + 1 : 0;
+  const long long base = (long long)w0 + b;
 
   float m = -INFINITY;
-  for (int i = tid; i < n; i += NT) m = fmaxf(m, p.ws_ml[(base + i) * 2]);
+  for (int i = tid; i < n; i += NT) m = fmaxf(m, p.ws_ml[((base + i) * p.Hq + h) * 2]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
   if (lane == 0) wmax[wave] = m;
@@ -368,31 +377,35 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) 
   for (int w = 1; w < NT / 64; ++w) mstar = fmaxf(mstar, wmax[w]);
   const float mref = mstar == -INFINITY ? 0.f : mstar;
 
-  const int d = tid % D;
-  const int cg = tid / D;
-  float acc = 0.f, lsum = 0.f;
+  const int sub = tid % TPR;   // float4 column group
+  const int rg = tid / TPR;    // partial within a pass
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
 #pragma unroll 4
-  for (int i = cg; i < n; i += CG) {
-    const float e = fast_exp2(p.ws_ml[(base + i) * 2] - mref);
-    acc += e * p.ws_o[(base + i) * D + d];
-    lsum += e * p.ws_ml[(base + i) * 2 + 1];
+  for (int i = rg; i < n; i += RPP) {
+    const long long r = (base + i) * p.Hq + h;
+    const float e = fast_exp2(p.ws_ml[r * 2] - mref);
+    const f32x4 o4 = *reinterpret_cast<const f32x4*>(p.ws_o + r * D + sub * 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += e * o4[u];
+    lsum += e * p.ws_ml[r * 2 + 1];
   }
   red[tid] = acc;
+  if (sub == 0) lred[rg] = lsum;
   __syncthreads();
-  if (cg == 0) {
+  if (rg == 0) {
 #pragma unroll
-    for (int g = 1; g < CG; ++g) acc += red[g * D + d];
-  }
-  __syncthreads();
-  red[tid] = lsum;
-  __syncthreads();
-  if (cg == 0) {
+    for (int g = 1; g < RPP; ++g) {
+      const f32x4 x = red[g * TPR + sub];
 #pragma unroll
-    for (int g = 1; g < CG; ++g) lsum += red[g * D + d];
+      for (int u = 0; u < 4; ++u) acc[u] += x[u];
+      lsum += lred[g];
+    }
     // A row with no keys has lsum == 0 and returns 0; NaN inputs stay NaN.
-    const float r = lsum != 0.f ? acc / lsum : 0.f;
-    const T w = (T)r;
-    p.out[((long long)b * p.Hq + h) * D + d] = __builtin_bit_cast(uint16_t, w);
+    typename Mfma<T>::v4 w;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = (T)(lsum != 0.f ? acc[u] / lsum : 0.f);
+    *reinterpret_cast<uint2*>(p.out + ((long long)b * p.Hq + h) * D + sub * 4) = __builtin_bit_cast(uint2, w);
   }
 }
 

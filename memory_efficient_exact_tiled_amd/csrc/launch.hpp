@@ -39,10 +39,10 @@ struct DecParams {
   uint16_t* out;
   const float* slopes;
   int* plan;             // [B + 2]: prefix sums of the clamped ctx, then the span L
-  float* ws_o;           // [B][Hq][nsplit][D] unnormalised partial outputs
-  float* ws_ml;          // [B][Hq][nsplit][2] partial (row max in log2 units, row sum)
-  int B, Hq, Hkv, group, S_max, nsplit, nhb;
-  int grid;              // split work-groups along x (one per compute unit)
+  float* ws_o;           // [rows][Hq][D] unnormalised partial outputs; row = w + b
+  float* ws_ml;          // [rows][Hq][2] partial (row max in log2 units, row sum)
+  int B, Hq, Hkv, group, S_max, nhb;
+  int grid;              // split work-groups along x: min(compute units, kDecodeMaxSplit)
   int alibi;
   float scale_log2;
 };
@@ -81,7 +81,8 @@ struct BwdParams {
 // the shortest span of keys of a decode split work-group.
 int fwd_block_m(int D, bool causal, bool block_sparse, bool wide);
 constexpr int kSparseBlock = 64;   // block edge of block-sparse masks
-constexpr int kDecodeChunk = 512;
+constexpr int kDecodeChunk = 64;        // shortest span of keys of a split work-group
+constexpr int kDecodeMaxSplit = 1024;   // most split work-groups (the workspace holds that many + B rows)
 
 struct AppendParams {
   uint16_t* kc;

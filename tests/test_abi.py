@@ -37,15 +37,15 @@ def test_strerror_and_supported():
 
 
 def test_workspace_bytes():
-    C = mea.decode_chunk()
-    assert C == 512
-    # plan header [B + 2] int32, then partials [B][Hq][nsplit][D] and their
-    # (max, sum) pairs, each part 256-byte aligned; a sequence is covered by
-    # at most ceil(S_max / C) + 1 spans of at least C keys
-    nsplit = (32768 + C - 1) // C + 1
-    o = 32 * 32 * nsplit * 128 * 4
+    assert mea.decode_chunk() == 64
+    # plan header [B + 2] int32, then partials [1024 + B][Hq][D] and their
+    # (max, sum) pairs, each part 256-byte aligned; independent of S_max
+    rows = 1024 + 32
+    o = rows * 32 * 128 * 4
     head = ((32 + 2) * 4 + 255) // 256 * 256
-    assert mea.decode_workspace_bytes(32, 32, 128, 32768) == head + ((o + 255) // 256) * 256 + 32 * 32 * nsplit * 2 * 4
+    want = head + ((o + 255) // 256) * 256 + rows * 32 * 2 * 4
+    assert mea.decode_workspace_bytes(32, 32, 128, 32768) == want
+    assert mea.decode_workspace_bytes(32, 32, 128, 1) == want
     assert mea.decode_workspace_bytes(0, 32, 128, 32768) == 0
 
 
