@@ -54,6 +54,7 @@ namespace {
 constexpr int kWaves = 8;      // (KV head, head block) units per work-group
 constexpr int kKStep = 16;     // keys per wave step
 constexpr int kStages = 2;     // register stages of K/V per wave
+constexpr int kInlinePlan = 512;   // batches up to this size are planned inside the split kernel
 
 template <int D, int KSTEP>
 struct DecShape {
@@ -63,12 +64,52 @@ struct DecShape {
   static constexpr int NLD = KSTEP * CPR / 64;     // V chunks per lane per step
 };
 
+// One wave: prefix sums of the clamped context lengths, then the span L,
+// into dst[0 .. B + 1]. Lane i takes sequences [i * per, (i + 1) * per): it
+// sums them, a wave-wide shuffle scan gives each lane its starting offset,
+// and a second pass writes the running sums (no LDS, no barrier).
+__device__ __forceinline__ void plan_wave(const DecParams& p, int* dst, int lane) {
+  const int per = (p.B + 63) / 64;
+  const int b0 = lane * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < p.B) sum += min(max(p.ctx[b], 0), p.S_max);
+  }
+  int x = sum;   // inclusive scan over the lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  int run = x - sum;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < p.B) {
+      run += min(max(p.ctx[b], 0), p.S_max);
+      dst[b + 1] = run;
+    }
+  }
+  if (lane == 0) dst[0] = 0;
+  if (lane == 63) {
+    const long long per_wg = ((long long)x + p.grid - 1) / p.grid;   // x: the total at the last lane
+    const long long L = max((long long)kDecodeChunk, (per_wg + 15) / 16 * 16);
+    dst[p.B + 1] = (int)min(L, (long long)0x7fffffff);
+  }
+}
+
+// The plan as a kernel of its own (batches of more than kInlinePlan
+// sequences; smaller ones are planned inside the split kernel).
+__global__ void __launch_bounds__(64) decode_plan_kernel(const DecParams p) {
+  plan_wave(p, p.plan, threadIdx.x);
+}
+
 // One wave = one (KV head g, block of up to 16 of g's query heads) over the
 // work-group's span of keys; the waves of a work-group take consecutive
 // units, so they read the same cache rows at the same time. KSTEP keys per step (16 or 32);
 // STAGES register stages of K/V: the loads of the next STAGES-1 steps are in
 // flight while the current step is computed.
-template <typename T, int D, int KSTEP, int STAGES>
+template <typename T, int D, int KSTEP, int STAGES, bool INLINE_PLAN>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(const DecParams p) {
   using S = DecShape<D, KSTEP>;
@@ -85,11 +126,24 @@ decode_split_kernel(const DecParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // [B + 1] prefix sums of ctx, then L: from the plan kernel, or (small
+  // batches) computed here by wave 0 into LDS, work-group (0, 0) also
+  // storing it for the combine.
+  const int* prefix = p.plan;
+  if constexpr (INLINE_PLAN) {
+    __shared__ int splan[kInlinePlan + 2];
+    if (wave == 0) {
+      plan_wave(p, splan, lane);
+      if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = lane; i < p.B + 2; i += 64) p.plan[i] = splan[i];
+    }
+    __syncthreads();
+    prefix = splan;
+  }
   const int unit = blockIdx.y * kWaves + wave;
   if (unit >= p.Hkv * p.nhb) return;
   const int g = unit / p.nhb;
   const int hb = unit - g * p.nhb;
-  const int* prefix = p.plan;              // [B + 1] prefix sums of ctx, then L
   const int total = prefix[p.B];
   const int L = prefix[p.B + 1];
   const long long lo64 = (long long)blockIdx.x * L;
@@ -305,41 +359,6 @@ decode_split_kernel(const DecParams p) {
   }   // sequences of the range
 }
 
-// One wave: prefix sums of the clamped context lengths, then the span L.
-// Lane i takes sequences [i * per, (i + 1) * per): it sums them, a wave-wide
-// shuffle scan gives each lane its starting offset, and a second pass writes
-// the running sums (no LDS, no barrier).
-__global__ void __launch_bounds__(64) decode_plan_kernel(const DecParams p) {
-  const int lane = threadIdx.x;
-  const int per = (p.B + 63) / 64;
-  const int b0 = lane * per;
-  int sum = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = b0 + i;
-    if (b < p.B) sum += min(max(p.ctx[b], 0), p.S_max);
-  }
-  int x = sum;   // inclusive scan over the lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  int run = x - sum;
-  for (int i = 0; i < per; ++i) {
-    const int b = b0 + i;
-    if (b < p.B) {
-      run += min(max(p.ctx[b], 0), p.S_max);
-      p.plan[b + 1] = run;
-    }
-  }
-  if (lane == 0) p.plan[0] = 0;
-  if (lane == 63) {
-    const long long per_wg = ((long long)x + p.grid - 1) / p.grid;   // x: the total at the last lane
-    const long long L = max((long long)kDecodeChunk, (per_wg + 15) / 16 * 16);
-    p.plan[p.B + 1] = (int)min(L, (long long)0x7fffffff);
-  }
-}
-
 // One work-group of 256 threads per (sequence, query head). A partial's
 // output row (D floats) is read by D / 4 threads, 16 bytes each, so a pass
 // merges 1024 / D partials at once: thread t takes the float4 t % (D / 4) of
@@ -412,11 +431,16 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const DecParams p) 
 template <typename T, int D>
 hipError_t launch_typed(const DecParams& p, hipStream_t stream) {
   const int units = p.Hkv * p.nhb;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(64), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages>), dim3(p.grid, (units + kWaves - 1) / kWaves),
-                     dim3(kWaves * 64), 0, stream, p);
+  const dim3 grid(p.grid, (units + kWaves - 1) / kWaves);
+  hipError_t e;
+  if (p.B <= kInlinePlan) {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages, true>), grid, dim3(kWaves * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(64), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_split_kernel<T, D, kKStep, kStages, false>), grid, dim3(kWaves * 64), 0, stream, p);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq, p.B), dim3(256), 0, stream, p);

@@ -32,6 +32,9 @@ SMALL = [
     # plan's 256-wide scan steps
     ("batch_300_scan_carry", 8, [int(x) for x in np.random.default_rng(8).integers(0, 60, 300)], 64, 2, 1, 64,
      "fp16", False),
+    # more than 512 sequences: planned by the separate plan kernel
+    ("batch_600_plan_kernel", 9, [int(x) for x in np.random.default_rng(9).integers(0, 20, 600)], 32, 2, 1, 64,
+     "bf16", False),
     # more keys than 512 per compute unit: spans longer than the chunk,
     # crossing sequence boundaries mid-span
     ("long_spans", 7, [70000, 70001, 1, 9000], 70001, 4, 1, 64, "fp16", True),
