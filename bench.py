@@ -434,9 +434,9 @@ def main():
         "roofline_decode": None if dec_gbs is None else {
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic_for(traffic, "decode_plan_kernel", "decode_split_kernelIDF16bLi128",
-                                   "decode_combine_kernelIDF16bLi128"),
-            "kernel": "decode_plan_kernel + decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>",
+            # At B=32 the plan runs inside the split kernel (no plan launch).
+            "traffic": traffic_for(traffic, "decode_split_kernelIDF16bLi128", "decode_combine_kernelIDF16bLi128"),
+            "kernel": "decode_split_kernel<bf16,128> (plan inside) + decode_combine_kernel<bf16,128>",
             "avg_launch_us": round(ms["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes,
             "alone": None if "decode" not in alone else {
                 "launches_back_to_back": ALONE, "avg_launch_us": round(alone["decode"] * 1e3, 2),

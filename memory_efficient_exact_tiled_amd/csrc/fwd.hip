@@ -523,25 +523,42 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   }
 
   // ---- epilogue --------------------------------------------------------------
+  // The normalised tile is staged through LDS (the K/V buffers, free once
+  // every wave has left the loop) so that the stores to HBM are whole rows,
+  // 16 bytes per lane, instead of 8-byte pieces of 32 rows per instruction:
+  // the same bytes, half the store instructions (measured 1-5 % faster, most
+  // on packed batches of short tiles).
+  __syncthreads();
+  constexpr int OS = D + 8;   // staged row stride (elements)
+  static_assert(kWaves * QW * OS <= 2 * TILE, "the staged output must fit the K/V buffers");
+  uint16_t* ob = smem + wave * (QW * OS);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const int qi = wq0 + qb * 32 + l32;
-    if (qi < M_s) {
-      const float inv = lt != 0.f ? 1.f / lt : 0.f;   // no allowed key -> 0; NaN stays NaN
-      uint16_t* orow = p.out + qoff + (long long)qi * p.q_rstride;
+    const float inv = lt != 0.f ? 1.f / lt : 0.f;   // no allowed key -> 0; NaN stays NaN
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          typename MF::v4 w;
+      for (int rg = 0; rg < 4; ++rg) {
+        typename MF::v4 w;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) w[u] = (T)(o[qb][db][rg * 4 + u] * inv);
-          *reinterpret_cast<uint2*>(orow + db * 32 + rg * 8 + hi * 4) = __builtin_bit_cast(uint2, w);
-        }
-      if (p.lse != nullptr && hi == 0)
-        p.lse[lse_off + qi] = lt != 0.f ? (m_run[qb] + __log2f(lt)) * kLn2 : -INFINITY;
-    }
+        for (int u = 0; u < 4; ++u) w[u] = (T)(o[qb][db][rg * 4 + u] * inv);
+        *reinterpret_cast<uint2*>(ob + (qb * 32 + l32) * OS + db * 32 + rg * 8 + hi * 4) = __builtin_bit_cast(uint2, w);
+      }
+    if (qi < M_s && p.lse != nullptr && hi == 0)
+      p.lse[lse_off + qi] = lt != 0.f ? (m_run[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+  __builtin_amdgcn_wave_barrier();   // each wave reads back only its own rows
+  constexpr int CPO = D / 8;         // 16-byte chunks per output row
+#pragma unroll
+  for (int i = 0; i < QW * CPO / 64; ++i) {
+    const int ch = lane + i * 64;
+    const int r = ch / CPO;
+    const int cc = (ch - r * CPO) * 8;
+    const int qi = wq0 + r;
+    const uint4 v = *reinterpret_cast<const uint4*>(ob + r * OS + cc);
+    if (qi < M_s) *reinterpret_cast<uint4*>(p.out + qoff + (long long)qi * p.q_rstride + cc) = v;
   }
 }
 
