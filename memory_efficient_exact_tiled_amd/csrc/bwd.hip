@@ -344,17 +344,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     __builtin_amdgcn_s_setprio(0);
   }
 
-  if (qin) {
-    uint16_t* orow = p.dq + qoff + (long long)qi * p.q_rstride;
+  // dQ is staged through the (then free) K/V buffers and stored as whole
+  // rows, 16 bytes per lane, as in the forward's epilogue.
+  __syncthreads();
+  constexpr int OS = D + 8;
+  static_assert(kWaves * QW * OS <= 2 * 2 * TILE, "the staged dQ must fit the K/V buffers");
+  uint16_t* ob = smem + wave * (QW * OS);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        typename MF::v4 w;
+    for (int rg = 0; rg < 4; ++rg) {
+      typename MF::v4 w;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = (T)(acc[db][rg * 4 + u] * p.scale);
-        *reinterpret_cast<uint2*>(orow + db * 32 + rg * 8 + hi * 4) = __builtin_bit_cast(uint2, w);
-      }
+      for (int u = 0; u < 4; ++u) w[u] = (T)(acc[db][rg * 4 + u] * p.scale);
+      *reinterpret_cast<uint2*>(ob + l32 * OS + db * 32 + rg * 8 + hi * 4) = __builtin_bit_cast(uint2, w);
+    }
+  __builtin_amdgcn_wave_barrier();   // each wave reads back only its own rows
+  constexpr int CPO = D / 8;
+#pragma unroll
+  for (int i = 0; i < QW * CPO / 64; ++i) {
+    const int ch = lane + i * 64;
+    const int r = ch / CPO;
+    const int cc = (ch - r * CPO) * 8;
+    const int q = wq0 + r;
+    const uint4 v = *reinterpret_cast<const uint4*>(ob + r * OS + cc);
+    if (q < M_s) *reinterpret_cast<uint4*>(p.dq + qoff + (long long)q * p.q_rstride + cc) = v;
   }
 }
 
@@ -611,22 +625,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     }
   }
 
-  if (kin) {
-    const long long e = koff + (long long)kj * p.kv_rstride;
+  // dK and dV are staged through the (then free) Q/dO buffers and stored as
+  // whole rows, 16 bytes per lane, as in the forward's epilogue.
+  __syncthreads();
+  constexpr int OS = D + 8;
+  static_assert(kWaves * 2 * KW * OS <= 2 * 2 * TILE, "the staged dK, dV must fit the Q/dO buffers");
+  uint16_t* obk = smem + wave * (2 * KW * OS);
+  uint16_t* obv = obk + KW * OS;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        typename MF::v4 wk, wv;
+    for (int rg = 0; rg < 4; ++rg) {
+      typename MF::v4 wk, wv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          wk[u] = (T)(dka[db][rg * 4 + u] * p.scale);
-          wv[u] = (T)dva[db][rg * 4 + u];
-        }
-        const int col = db * 32 + rg * 8 + hi * 4;
-        *reinterpret_cast<uint2*>(p.dk + e + col) = __builtin_bit_cast(uint2, wk);
-        *reinterpret_cast<uint2*>(p.dv + e + col) = __builtin_bit_cast(uint2, wv);
+      for (int u = 0; u < 4; ++u) {
+        wk[u] = (T)(dka[db][rg * 4 + u] * p.scale);
+        wv[u] = (T)dva[db][rg * 4 + u];
       }
+      const int col = db * 32 + rg * 8 + hi * 4;
+      *reinterpret_cast<uint2*>(obk + l32 * OS + col) = __builtin_bit_cast(uint2, wk);
+      *reinterpret_cast<uint2*>(obv + l32 * OS + col) = __builtin_bit_cast(uint2, wv);
+    }
+  __builtin_amdgcn_wave_barrier();   // each wave reads back only its own rows
+  constexpr int CPO = D / 8;
+#pragma unroll
+  for (int i = 0; i < KW * CPO / 64; ++i) {
+    const int ch = lane + i * 64;
+    const int r = ch / CPO;
+    const int cc = (ch - r * CPO) * 8;
+    const int kk = wj0 + r;
+    const uint4 vk = *reinterpret_cast<const uint4*>(obk + r * OS + cc);
+    const uint4 vv = *reinterpret_cast<const uint4*>(obv + r * OS + cc);
+    if (kk < N_s) {
+      const long long e = koff + (long long)kk * p.kv_rstride + cc;
+      *reinterpret_cast<uint4*>(p.dk + e) = vk;
+      *reinterpret_cast<uint4*>(p.dv + e) = vv;
+    }
   }
 }
 
