@@ -56,19 +56,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_code_hash(text):
+    """sha256[:16] of a kernel source with comments and blank lines removed: the
+    fingerprint of the code the counters were taken on (a comment edit keeps it)."""
+    import hashlib
+    import re
+    t = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    t = re.sub(r"//[^\n]*", "", t)
+    lines = [ln.rstrip() for ln in t.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def measured_traffic():
     """HBM bytes per launch from profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE
     and WRITE_SIZE, calibrated against a plain 1 GiB copy), or None for every
-    kernel once a kernel source differs from the one the counters were taken on."""
-    import hashlib
+    kernel once a kernel's code differs from the one the counters were taken on."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
     csrc = os.path.join(ROOT, "memory_efficient_exact_tiled_amd", "csrc")
-    for name, sha in t["sources_sha256_16"].items():
-        cur = hashlib.sha256(open(os.path.join(csrc, name)).read().encode()).hexdigest()[:16]
-        if cur != sha:
+    for name, sha in t["code_sha256_16"].items():
+        if kernel_code_hash(open(os.path.join(csrc, name)).read()) != sha:
             return None
     out = {}
     for k, v in t["kernels"].items():

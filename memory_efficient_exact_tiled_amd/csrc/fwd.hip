@@ -13,8 +13,8 @@
 //     segment, query head); wave w owns 32 * QB consecutive rows (QB = 2 for
 //     dense D=64 when that still gives two work-groups per compute unit,
 //     else 1); two waves (three at QB=1, D=64) share each SIMD, so one
-//     wave's softmax overlaps another's matrix-core work; MFMA phases run at
-//     raised wave priority;
+//     wave's softmax overlaps another's matrix-core work; the P.V products
+//     (and at D=64 the score products) run at raised wave priority;
 //   * K/V blocks of BN = 64 keys are copied to LDS with buffer loads whose
 //     resource ends at the segment's last key (rows past it read as zeros):
 //     straight into LDS (LDS DMA) at D=128, through registers at D=64 (the
@@ -48,6 +48,7 @@
 //     work-group walks only the key blocks at least one of its query blocks
 //     has on (a skip list read from the mask), and a wave skips the blocks
 //     that are off for its own query block.
+//   * the normalised output is staged through LDS and stored as whole rows.
 //
 // Launch order: work-group p runs on XCD p % 8. Without a causal mask each
 // XCD is given a contiguous range of logical work-groups, so the query tiles
