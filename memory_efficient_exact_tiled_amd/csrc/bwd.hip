@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  uint4 kst[NLD], vst[NLD];
+  uint4 kst[2][NLD], vst[2][NLD];
   const uint32_t row_bytes = (uint32_t)p.kv_rstride * 2u;
   uint32_t ld_off[NLD];
 #pragma unroll
@@ -222,25 +222,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     const int r = ch / CPR;
     ld_off[i] = (uint32_t)r * row_bytes + (uint32_t)(ch - r * CPR) * 16u;
   }
-  auto gload = [&](int kt) {
-    const uint32_t bytes = rows_bytes(N_s - kt * BN, row_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + koff + (long long)kt * BN * p.kv_rstride, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + koff + (long long)kt * BN * p.kv_rstride, bytes);
+  // A block index outside [0, ntiles) gives an empty resource: the loads
+  // are still issued but return zeros without touching memory.
+  auto gload = [&](int kt, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+    const bool in = kt >= 0 && kt < ntiles;
+    const long long o = in ? koff + (long long)kt * BN * p.kv_rstride : 0;
+    const uint32_t bytes = in ? rows_bytes(N_s - kt * BN, row_bytes) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + o, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + o, bytes);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      kst[i] = buf_load16(rk, ld_off[i]);
-      vst[i] = buf_load16(rv, ld_off[i]);
+      kr[i] = buf_load16(rk, ld_off[i]);
+      vr[i] = buf_load16(rv, ld_off[i]);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const uint4 (&kr)[NLD], const uint4 (&vr)[NLD]) {
     uint16_t* ks = smem + buf * 2 * TILE;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int ch = tid + i * (kWaves * 64);
       const int r = ch / CPR;
       const int cc = (ch - r * CPR) * 8;
-      *reinterpret_cast<uint4*>(ks + lds_at<D>(r, cc)) = kst[i];
-      *reinterpret_cast<uint4*>(ks + TILE + lds_at<D>(r, cc)) = vst[i];
+      *reinterpret_cast<uint4*>(ks + lds_at<D>(r, cc)) = kr[i];
+      *reinterpret_cast<uint4*>(ks + TILE + lds_at<D>(r, cc)) = vr[i];
     }
   };
 
@@ -265,18 +269,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     return on;
   };
   auto next_tile = [&](int kt) { return BS ? skip.next_on(kt, ntiles, tile_on) : kt; };
-  int kt0 = next_tile(0), nkt = 0;
-  if (kt0 < ntiles) gload(kt0);
-  for (int kt = kt0, n = 0; kt < ntiles; kt = nkt, ++n) {
-    const int buf = BS ? (n & 1) : (kt & 1);
-    nkt = next_tile(kt + 1);
-    lstore(buf);
-    __syncthreads();
-    if (nkt < ntiles) gload(nkt);
-
+  // One key block on LDS buffer buf.
+  auto compute = [&](const int kt, const int buf) {
     const int key_base = kt * BN;
-    if (key_base >= wkend) continue;
-    if (BS && (wqblk < 0 || p.block_mask[(long long)wqblk * p.nkb + kt] == 0)) continue;
+    if (key_base >= wkend) return;
+    if (BS && (wqblk < 0 || p.block_mask[(long long)wqblk * p.nkb + kt] == 0)) return;
     const uint16_t* Ks = smem + buf * 2 * TILE;
     const uint16_t* Vs = Ks + TILE;
 
@@ -342,6 +339,41 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
                             dsf[tt], acc[db]);
       }
     __builtin_amdgcn_s_setprio(0);
+  };
+
+  int kt0 = next_tile(0), nkt = 0;
+  if constexpr (BS == 0) {
+    // Two blocks ahead, in two register sets, over pairs of blocks, as in the
+    // forward (every path back to the loop head has issued both sets' loads).
+    gload(kt0, kst[0], vst[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(kt0 + 1, kst[1], vst[1]);
+    int kt = kt0;
+    for (; kt + 1 < ntiles; kt += 2) {
+      lstore(0, kst[0], vst[0]);
+      __syncthreads();
+      gload(kt + 2, kst[0], vst[0]);
+      compute(kt, 0);
+      lstore(1, kst[1], vst[1]);
+      __syncthreads();
+      gload(kt + 3, kst[1], vst[1]);
+      compute(kt + 1, 1);
+    }
+    if (kt < ntiles) {
+      lstore(0, kst[0], vst[0]);
+      __syncthreads();
+      compute(kt, 0);
+    }
+  } else {
+    if (kt0 < ntiles) gload(kt0, kst[0], vst[0]);
+    for (int kt = kt0, n = 0; kt < ntiles; kt = nkt, ++n) {
+      const int buf = n & 1;
+      nkt = next_tile(kt + 1);
+      lstore(buf, kst[0], vst[0]);
+      __syncthreads();
+      if (nkt < ntiles) gload(nkt, kst[0], vst[0]);
+      compute(kt, buf);
+    }
   }
 
   // dQ is staged through the (then free) K/V buffers and stored as whole
