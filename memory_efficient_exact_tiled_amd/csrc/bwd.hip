@@ -15,7 +15,8 @@
 //     caller's workspace (+inf for a row with no allowed key, so its P is 0);
 //   * bwd_dq_kernel: the forward's shape. A work-group owns 128 query rows of
 //     one (segment, query head), keeps Q and dO in registers and streams K/V
-//     blocks of 64 keys through LDS. S^T = K Q^T and dP^T = V dO^T leave one
+//     blocks of 64 keys through LDS (loaded two blocks ahead without a
+//     block-sparse mask). S^T = K Q^T and dP^T = V dO^T leave one
 //     query per lane, so lse and Delta are per-lane scalars; dS^T is rounded
 //     to the input type and fed as the B operand of dQ^T += K^T dS^T, with K^T
 //     read from the row-major K block by ds_read_b64_tr_b16;

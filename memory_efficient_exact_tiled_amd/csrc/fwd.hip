@@ -20,7 +20,8 @@
 //     straight into LDS (LDS DMA) at D=128, through registers at D=64 (the
 //     faster of the two for each); double buffered so one barrier per block
 //     suffices, with the next block's copies in flight during the current
-//     block's compute (two blocks ahead for the register staging);
+//     block's compute (two blocks ahead for the register staging of
+//     launches without a block-sparse mask);
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
 //     registers for the whole kernel). With this orientation each lane holds
 //     one query's scores for 32 of the 64 keys, so the row max needs a single
