@@ -101,6 +101,22 @@ def test_dense_wide_tiles_ragged(mea, dt, alibi):
         assert report(f"{name} b{b}", got[b, rows], want, TOL[dt]) <= TOL[dt]
 
 
+@pytest.mark.parametrize("N", [1, 64, 65, 128, 129, 192, 193])
+def test_dense_wide_tiles_few_key_blocks(mea, N):
+    """The 256-row work-groups (B*Hq*ceil(M/256) >= 512) walk their key blocks
+    in pairs with a single-block tail; 1 to 4 blocks, full and ragged, cover
+    an empty pair loop, one pair, a pair plus tail and two pairs."""
+    B, M, Hq, Hkv = 8, 1000, 16, 4
+    say(f"case wide_few_blocks_n{N}")
+    c = inp.dense_case(78, B, M, N, Hq, Hkv, 64, "bf16")
+    out, _, scale = _run(mea, c, "bf16")
+    got = host_f64(out)
+    rows = np.array([0, 63, 64, 255, 256, 600, 999])
+    for b in (0, 5):
+        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], "bf16", scale, b, rows)
+        assert report(f"wide_n{N} b{b}", got[b, rows], want, TOL["bf16"]) <= TOL["bf16"]
+
+
 def test_varlen_gqa_alibi_full_config(mea):
     """8 packed segments, lengths uniform in [64, 2048] (seeded), Hq=32, Hkv=8,
     D=128, bf16, block-diagonal causal + ALiBi: sampled rows of every segment."""
