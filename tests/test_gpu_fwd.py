@@ -102,19 +102,22 @@ def test_dense_wide_tiles_ragged(mea, dt, alibi):
 
 
 @pytest.mark.parametrize("N", [1, 64, 65, 128, 129, 192, 193])
-def test_dense_wide_tiles_few_key_blocks(mea, N):
+@pytest.mark.parametrize("dt,alibi", [("bf16", False), ("fp16", True)])
+def test_dense_wide_tiles_few_key_blocks(mea, N, dt, alibi):
     """The 256-row work-groups (B*Hq*ceil(M/256) >= 512) walk their key blocks
     in pairs with a single-block tail; 1 to 4 blocks, full and ragged, cover
     an empty pair loop, one pair, a pair plus tail and two pairs."""
     B, M, Hq, Hkv = 8, 1000, 16, 4
-    say(f"case wide_few_blocks_n{N}")
-    c = inp.dense_case(78, B, M, N, Hq, Hkv, 64, "bf16")
-    out, _, scale = _run(mea, c, "bf16")
+    name = f"wide_few_blocks_n{N}_{dt}{'_alibi' if alibi else ''}"
+    say(f"case {name}")
+    c = inp.dense_case(78, B, M, N, Hq, Hkv, 64, dt)
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    out, _, scale = _run(mea, c, dt, slopes=slopes)
     got = host_f64(out)
     rows = np.array([0, 63, 64, 255, 256, 600, 999])
     for b in (0, 5):
-        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], "bf16", scale, b, rows)
-        assert report(f"wide_n{N} b{b}", got[b, rows], want, TOL["bf16"]) <= TOL["bf16"]
+        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], dt, scale, b, rows, alibi_slopes=slopes)
+        assert report(f"{name} b{b}", got[b, rows], want, TOL[dt]) <= TOL[dt]
 
 
 def test_varlen_gqa_alibi_full_config(mea):
