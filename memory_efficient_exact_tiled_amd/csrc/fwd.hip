@@ -114,6 +114,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   constexpr int CPR = S::CPR, NLD = S::NLD;
   constexpr int DB = D / 32;   // 32-wide output column blocks
   constexpr int DS = D / 16;   // k-steps of the score product
+  constexpr bool kFastSum = D == 64 && QB_ == 1 && CS == 1 && AL == 0 && BS == 0;
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE];
 
@@ -461,48 +462,85 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
           }
         cc = 1.f;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      {
-        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-      }
-      const float mt = fmaf(mx, cc, bb);
-      if (__any(mt > m_run[qb] + kRescaleThreshold)) {
-        const float mn = fmaxf(m_run[qb], mt);
-        const float alpha = fast_exp2(m_run[qb] - (mn == -INFINITY ? 0.f : mn));
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-        m_run[qb] = mn;
-      }
-      const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(fmaf(s[qb][kb][r], cc, bb - mu));
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pf[qb][tt][u] = (T)s[qb][tt >> 1][(tt & 1) * 8 + u];
-      // Row sum of the rounded P (the values P.V uses), two at a time.
+      // Under the compile-time causal mask at D=64 (no ALiBi, no block mask)
+      // P is first tried with the running max as the offset, before this
+      // block's max is known. If every rounded P of the lane is below 2^7
+      // (lane row sum below 128; NaN and inf fail the test), no score is
+      // more than the rescale threshold above the running max, so the full
+      // step below would keep that max and produce this same P. Only the
+      // order of the row-sum additions differs. The full step runs when the
+      // test fails: on a row's first block (running max -inf) and when the
+      // max jumps. Measured 3-5 % faster on the causal B=4 M=4096 launch;
+      // slower for QB=2, at D=128 and with ALiBi, whose rising bias fails
+      // the test on most blocks.
       float psum = 0.f;
+      bool full = true;
+      if constexpr (kFastSum) {
+        const float nb = bb - m_run[qb];
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        typedef T T2 __attribute__((ext_vector_type(2)));
-        const T2 one2 = {(T)1.f, (T)1.f};
+        for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-        for (int u = 0; u < 8; u += 2) {
-          const T2 pp = {pf[qb][tt][u], pf[qb][tt][u + 1]};
-          if constexpr (sizeof(T) == 2 && __is_same(T, __bf16))
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
-          else
-            psum = __builtin_amdgcn_fdot2(pp, one2, psum, false);
+          for (int u = 0; u < 8; ++u) pf[qb][tt][u] = (T)fast_exp2(fmaf(s[qb][tt >> 1][(tt & 1) * 8 + u], cc, nb));
+          typedef T T2 __attribute__((ext_vector_type(2)));
+          const T2 one2 = {(T)1.f, (T)1.f};
+#pragma unroll
+          for (int u = 0; u < 8; u += 2) {
+            const T2 pp = {pf[qb][tt][u], pf[qb][tt][u + 1]};
+            float& acc = (tt & 1) ? ps1 : ps0;
+            if constexpr (sizeof(T) == 2 && __is_same(T, __bf16))
+              acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, acc, false);
+            else
+              acc = __builtin_amdgcn_fdot2(pp, one2, acc, false);
+          }
+        }
+        psum = ps0 + ps1;
+        full = !__all(psum < 128.f);
+      }
+      if (full) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        {
+          const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+        }
+        const float mt = fmaf(mx, cc, bb);
+        if (__any(mt > m_run[qb] + kRescaleThreshold)) {
+          const float mn = fmaxf(m_run[qb], mt);
+          const float alpha = fast_exp2(m_run[qb] - (mn == -INFINITY ? 0.f : mn));
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+          m_run[qb] = mn;
+        }
+        const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(fmaf(s[qb][kb][r], cc, bb - mu));
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) pf[qb][tt][u] = (T)s[qb][tt >> 1][(tt & 1) * 8 + u];
+        // Row sum of the rounded P (the values P.V uses), two at a time.
+        psum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          typedef T T2 __attribute__((ext_vector_type(2)));
+          const T2 one2 = {(T)1.f, (T)1.f};
+#pragma unroll
+          for (int u = 0; u < 8; u += 2) {
+            const T2 pp = {pf[qb][tt][u], pf[qb][tt][u + 1]};
+            if constexpr (sizeof(T) == 2 && __is_same(T, __bf16))
+              psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
+            else
+              psum = __builtin_amdgcn_fdot2(pp, one2, psum, false);
+          }
         }
       }
       l_run[qb] += psum;

@@ -285,3 +285,46 @@ def test_causal_alibi_extreme_slopes(mea, dt):
     assert np.all(np.isfinite(got))
     assert report(f"extreme slopes {dt}", got, want, TOL[dt]) <= TOL[dt]
     assert np.max(np.abs(lse.cpu().numpy() - wlse)) <= LSE_TOL[dt] * max(1.0, float(np.max(np.abs(wlse))) * 2 ** -11)
+
+
+def _bits_to_f32(bits, dt):
+    b = np.ascontiguousarray(bits)
+    if dt == "fp16":
+        return b.view(np.float16).astype(np.float32)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@pytest.mark.parametrize("dt,mode", [("bf16", "rising"), ("fp16", "rising"), ("bf16", "wide")])
+def test_causal_running_max_jumps(mea, dt, mode):
+    """Causal D=64 rows whose running max often jumps by more than 2^7 in P
+    from one key block to the next ("rising": key norms grow along the
+    sequence; "wide": scale 1, scores spread over tens of log2 units), next
+    to blocks where it does not. The forward may take P with the old running
+    max as the offset only when no P of the block reaches 2^7; both outcomes
+    occur in these inputs (checked below in fp64) and must agree with the
+    oracle."""
+    say(f"case causal running max jumps {dt} {mode}")
+    B, M, H, D = 2, 1000, 4, 64
+    c = inp.dense_case(91, B, M, M, H, H, D, dt)
+    scale = None
+    if mode == "rising":
+        grow = np.float32(1.0) + np.float32(8.0) * np.arange(M, dtype=np.float32) / np.float32(M)
+        c["k"] = inp.round_bits(_bits_to_f32(c["k"], dt) * grow[None, :, None, None], dt)
+    else:
+        scale = 1.0
+    sc = float(np.float32(1.0 / np.sqrt(D))) if scale is None else scale
+    # fp64 scores in log2 units; per (row, key block) the block max against
+    # the max over the earlier allowed keys.
+    q, k = _bits_to_f32(c["q"], dt).astype(np.float64), _bits_to_f32(c["k"], dt).astype(np.float64)
+    s = np.einsum("bmhd,bnhd->bhmn", q, k) * sc / np.log(2.0)
+    s = np.where(np.tril(np.ones((M, M), dtype=bool)), s, -np.inf)
+    nkb = (M + 63) // 64
+    bmax = np.stack([s[..., j * 64:(j + 1) * 64].max(-1) for j in range(nkb)], -1)
+    run = np.maximum.accumulate(bmax, -1)
+    jump = bmax[..., 1:] - run[..., :-1]
+    live = np.isfinite(bmax[..., 1:]) & np.isfinite(run[..., :-1])
+    assert np.any(live & (jump > 7.5)) and np.any(live & (jump < 0.0))
+    out, lse, sc = _run(mea, c, dt, causal=True, scale=scale, with_lse=True)
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, sc, causal=True)
+    assert report(f"running max jumps {dt} {mode}", host_f64(out), want, TOL[dt]) <= TOL[dt]
+    assert np.max(np.abs(lse.cpu().numpy() - wlse)) <= LSE_TOL[dt] * max(1.0, float(np.max(np.abs(wlse))) * 2 ** -11)
