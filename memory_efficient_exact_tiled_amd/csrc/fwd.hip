@@ -468,14 +468,14 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
       // (lane row sum below 128; NaN and inf fail the test), no score is
       // more than the rescale threshold above the running max, so the full
       // step below would keep that max and produce this same P. Only the
-      // order of the row-sum additions differs. The full step runs when the
-      // test fails: on a row's first block (running max -inf) and when the
-      // max jumps. Measured 3-5 % faster on the causal B=4 M=4096 launch;
+      // order of the row-sum additions differs. The full step runs directly
+      // while a row has no running max yet (its first block), and when the
+      // test fails. Measured 3-5 % faster on the causal B=4 M=4096 launch;
       // slower for QB=2, at D=128 and with ALiBi, whose rising bias fails
       // the test on most blocks.
       float psum = 0.f;
       bool full = true;
-      if constexpr (kFastSum) {
+      if (kFastSum && __all(m_run[qb] > -INFINITY)) {
         const float nb = bb - m_run[qb];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
