@@ -114,7 +114,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   constexpr int CPR = S::CPR, NLD = S::NLD;
   constexpr int DB = D / 32;   // 32-wide output column blocks
   constexpr int DS = D / 16;   // k-steps of the score product
-  constexpr bool kFastSum = D == 64 && QB_ == 1 && CS == 1 && AL == 0 && BS == 0;
+  constexpr bool kFastSum = D == 64 && BS == 0 && ((QB_ == 1 && CS == 1 && AL == 0) || QB_ == 2);
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE];
 
@@ -462,20 +462,21 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
           }
         cc = 1.f;
       }
-      // Under the compile-time causal mask at D=64 (no ALiBi, no block mask)
-      // P is first tried with the running max as the offset, before this
+      // At D=64 without ALiBi or a block mask (the causal QB=1 kernel, and
+      // the dense QB=2 kernel when its ALiBi flag is off), P is first tried
+      // with the running max as the offset, before this
       // block's max is known. If every rounded P of the lane is below 2^7
       // (lane row sum below 128; NaN and inf fail the test), no score is
       // more than the rescale threshold above the running max, so the full
       // step below would keep that max and produce this same P. Only the
       // order of the row-sum additions differs. The full step runs directly
       // while a row has no running max yet (its first block), and when the
-      // test fails. Measured 3-5 % faster on the causal B=4 M=4096 launch;
-      // slower for QB=2, at D=128 and with ALiBi, whose rising bias fails
-      // the test on most blocks.
+      // test fails. Measured 3-5 % faster on the causal and 2.4 % on the
+      // dense B=4 M=4096 launch; slower at D=128 and with ALiBi, whose
+      // rising bias fails the test on most blocks.
       float psum = 0.f;
       bool full = true;
-      if (kFastSum && __all(m_run[qb] > -INFINITY)) {
+      if (kFastSum && !ALIBI && __all(m_run[qb] > -INFINITY)) {
         const float nb = bb - m_run[qb];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll

@@ -328,3 +328,33 @@ def test_causal_running_max_jumps(mea, dt, mode):
     want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, sc, causal=True)
     assert report(f"running max jumps {dt} {mode}", host_f64(out), want, TOL[dt]) <= TOL[dt]
     assert np.max(np.abs(lse.cpu().numpy() - wlse)) <= LSE_TOL[dt] * max(1.0, float(np.max(np.abs(wlse))) * 2 ** -11)
+
+
+@pytest.mark.parametrize("dt,mode", [("bf16", "rising"), ("fp16", "wide")])
+def test_dense_wide_running_max_jumps(mea, dt, mode):
+    """The same jumps of the running max in the dense D=64 launch with
+    256-row work-groups (B*Hq*ceil(M/256) >= 512): sampled rows against the
+    oracle, after checking in fp64 that jumps above 2^7 and blocks below the
+    running max both occur."""
+    say(f"case dense wide running max jumps {dt} {mode}")
+    B, M, N, Hq, Hkv, D = 8, 1000, 1100, 16, 4, 64
+    c = inp.dense_case(92, B, M, N, Hq, Hkv, D, dt)
+    scale = None
+    if mode == "rising":
+        grow = np.float32(1.0) + np.float32(8.0) * np.arange(N, dtype=np.float32) / np.float32(N)
+        c["k"] = inp.round_bits(_bits_to_f32(c["k"], dt) * grow[None, :, None, None], dt)
+    else:
+        scale = 1.0
+    sc = float(np.float32(1.0 / np.sqrt(D))) if scale is None else scale
+    q = _bits_to_f32(c["q"][0], dt).astype(np.float64)
+    k = np.repeat(_bits_to_f32(c["k"][0], dt).astype(np.float64), Hq // Hkv, axis=1)
+    s = np.einsum("mhd,nhd->hmn", q, k) * sc / np.log(2.0)
+    bmax = np.stack([s[..., j * 64:(j + 1) * 64].max(-1) for j in range((N + 63) // 64)], -1)
+    jump = bmax[..., 1:] - np.maximum.accumulate(bmax, -1)[..., :-1]
+    assert np.any(jump > 7.5) and np.any(jump < 0.0)
+    out, _, sc = _run(mea, c, dt, scale=scale)
+    got = host_f64(out)
+    rows = np.array([0, 1, 31, 32, 63, 64, 255, 256, 511, 512, 767, 768, 998, 999])
+    for b in (0, 7):
+        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], dt, sc, b, rows)
+        assert report(f"dense jumps {dt} {mode} b{b}", got[b, rows], want, TOL[dt]) <= TOL[dt]
