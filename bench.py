@@ -67,22 +67,75 @@ def kernel_code_hash(text):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
+# Sources whose code decides what the counted kernels do (kernels, launch
+# shapes, host-side kernel and tile choices), and the compiler flags: the
+# stored traffic counts only while all of them are unchanged.
+TRAFFIC_SOURCES = ("api.hip", "fwd.hip", "bwd.hip", "decode.hip", "kvcache.hip", "common.hpp", "launch.hpp")
+
+
+def code_fingerprints(root=None):
+    """{source: kernel_code_hash} over TRAFFIC_SOURCES plus the build flags."""
+    import hashlib
+    root = ROOT if root is None else root
+    csrc = os.path.join(root, "memory_efficient_exact_tiled_amd", "csrc")
+    out = {name: kernel_code_hash(open(os.path.join(csrc, name)).read()) for name in TRAFFIC_SOURCES}
+    build_py = open(os.path.join(root, "memory_efficient_exact_tiled_amd", "build.py")).read()
+    flags = build_py[build_py.index("FLAGS = ["):]
+    flags = flags[:flags.index("]") + 1]
+    out["build.py FLAGS"] = hashlib.sha256(flags.encode()).hexdigest()[:16]
+    return out
+
+
 def measured_traffic():
     """HBM bytes per launch from profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE
     and WRITE_SIZE, calibrated against a plain 1 GiB copy), or None for every
-    kernel once a kernel's code differs from the one the counters were taken on."""
+    kernel once a source in TRAFFIC_SOURCES or the build flags differ from the
+    ones the counters were taken with."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    csrc = os.path.join(ROOT, "memory_efficient_exact_tiled_amd", "csrc")
-    for name, sha in t["code_sha256_16"].items():
-        if kernel_code_hash(open(os.path.join(csrc, name)).read()) != sha:
-            return None
+    if t.get("code_sha256_16") != code_fingerprints():
+        return None
     out = {}
     for k, v in t["kernels"].items():
         out[k] = v["fetch_bytes"] + v["write_bytes"]
     return out
+
+
+def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_path):
+    """Writes profiles/hbm_traffic.json from four rocprofv3 --pmc counter
+    collections (FETCH_SIZE and WRITE_SIZE of a bench run, then of
+    --copy-calibration): per kernel, the mean KiB per dispatch scaled by what
+    the same counter reads for the 1 GiB copy, with the code fingerprints."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    def copy_kib(path, counter):
+        vals = [v for k, (v, _) in per_kernel(path, counter).items() if "copyBuffer" in k]
+        return max(vals)
+
+    gib_kib = float(1 << 20)
+    ff = gib_kib / copy_kib(copy_fetch_csv, "FETCH_SIZE")
+    wf = gib_kib / copy_kib(copy_write_csv, "WRITE_SIZE")
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        if "mea" not in k:
+            continue
+        kernels[k] = {"fetch_bytes": fetch[k][0] * ff * 1024, "write_bytes": write[k][0] * wf * 1024,
+                      "dispatches": fetch[k][1]}
+    res = {"code_sha256_16": code_fingerprints(), "fetch_factor": ff, "write_factor": wf, "kernels": kernels}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
 
 
 def traffic_for(traffic, *needles):
@@ -101,7 +154,7 @@ def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def build_inputs(torch, inp):
+def build_inputs(torch, inp, with_decode=True):
     t0 = time.time()
     x = {}
     c = inp.dense_case(3, 4, 4096, 4096, 16, 16, 64, "bf16")
@@ -117,6 +170,10 @@ def build_inputs(torch, inp):
 
     B, S, Hq, Hkv, D = 32, 32768, 32, 8, 128
     ctx = inp.context_lengths(5, B, 1024, 32768)
+    if not with_decode:
+        # Decode is not among the items run: its 4.3 GB cache is not built.
+        x["decode"] = {"ctx_host": ctx}
+        return x
     kc = torch.empty((B, S, Hkv, D), dtype=torch.int16, device="cuda")
     vc = torch.empty_like(kc)
     poison = int(np.uint16(inp.POISON["bf16"]).view(np.int16))
@@ -139,31 +196,66 @@ def build_inputs(torch, inp):
     return x
 
 
-def cpu_baseline_fwd(c, seconds):
-    """fp64 oracle over blocks of 512 query rows (all 16 heads, all 4096 keys),
-    batch row by batch row, until about ``seconds`` have passed or the whole
-    workload is done."""
-    import oracle.attention as orc
+def host_description():
+    """The host the oracle runs on: logical CPUs, those this process may use,
+    and the CPU model (from /proc/cpuinfo)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": usable, "logical_cpus": os.cpu_count(), "cpu_model": model}
+
+
+def _blas_threads():
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
+def _fwd_sample(c, seconds, max_rows):
+    """fp64 oracle over blocks of 512 query rows (all 16 heads, all 4096 keys),
+    batch row by batch row, until about ``seconds`` have passed or max_rows
+    rows are done. Returns (rows, seconds)."""
+    import oracle.attention as orc
     rows_done, t0 = 0, time.time()
     scale = float(np.float32(1.0 / 8.0))
-    while rows_done < 4 * 4096 and time.time() - t0 < seconds:
+    while rows_done < max_rows and time.time() - t0 < seconds:
         b, r0 = divmod(rows_done, 4096)
         orc.fwd_rows(c["q"], c["k"], c["v"], "bf16", scale, b, np.arange(r0, r0 + 512))
         rows_done += 512
-    dt = time.time() - t0
-    flops = 4.0 * 16 * rows_done * 4096 * 64
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return rows_done, time.time() - t0
+
+
+def cpu_baseline_fwd(c, seconds):
+    """The oracle on the headline workload with every BLAS thread it gets (the
+    reported value), then one thread on a smaller sample."""
+    from threadpoolctl import threadpool_limits
+    threads = _blas_threads()
+    rows, dt = _fwd_sample(c, seconds, 4 * 4096)
+    flops = 4.0 * 16 * rows * 4096 * 64
+    with threadpool_limits(limits=1):
+        rows1, dt1 = _fwd_sample(c, seconds / 3, 4 * 4096)
+    flops1 = 4.0 * 16 * rows1 * 4096 * 64
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} of 16384 query rows (batch-major) x 16 heads x 4096 keys, no mask, "
-                      f"{flops / 1e9:.2f} GFLOP in {dt:.1f} s"}
+            "sample": f"{rows} of 16384 query rows (batch-major) x 16 heads x 4096 keys, no mask, "
+                      f"{flops / 1e9:.2f} GFLOP in {dt:.1f} s on {threads} BLAS threads",
+            "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s",
+                              "sample": f"{rows1} query rows x 16 heads x 4096 keys, {flops1 / 1e9:.2f} GFLOP "
+                                        f"in {dt1:.1f} s"},
+            "host": host_description()}
 
 
 def cpu_baseline_decode(ctx, seconds):
     """fp64 oracle decode of whole sequences (all 32 heads) until the time is up."""
     import mea_inputs as inp
     import oracle.attention as orc
-    from threadpoolctl import threadpool_info
     B, Hq, Hkv, D = 32, 32, 8, 128
     q = inp.normal_bits(5, (B, Hq, D), "bf16", 0)
     done, nbytes, busy = [], 0, 0.0
@@ -176,10 +268,11 @@ def cpu_baseline_decode(ctx, seconds):
         nbytes += int(ctx[b]) * Hkv * D * 2 * 2 + Hq * D * 2 * 2
         if busy >= seconds:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    threads = _blas_threads()
     return {"value": nbytes / busy / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(done)} whole sequences (ctx {[int(ctx[b]) for b in done]}), "
-                      f"{nbytes / 1e9:.3f} GB of K/V in {busy:.1f} s"}
+                      f"{nbytes / 1e9:.3f} GB of K/V in {busy:.1f} s on {threads} BLAS threads",
+            "host": host_description()}
 
 
 def naive_vs_mea_table(torch, inp, mea, B=4, H=16, D=64, seqlens=(512, 1024, 2048, 4096)):
@@ -257,7 +350,13 @@ def main():
                     help="reproduce the tutorial's naive-vs-memory-efficient table (ms, peak MB) for seqlen 512..4096")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (reference for HBM counters)")
+    ap.add_argument("--traffic-summary", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                            "COPY_WRITE_CSV", "OUT_JSON"),
+                    help="write the per-kernel HBM traffic file from rocprofv3 counter collections and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -283,13 +382,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30,
                           "launches": 5}), flush=True)
         return
-    x = build_inputs(torch, inp)
+    wanted = set(args.items.split(","))
+    x = build_inputs(torch, inp, with_decode="decode" in wanted)
     d, vl, dc = x["dense"], x["varlen"], x["decode"]
     ws = torch.empty(mea.decode_workspace_bytes(32, 32, 128, 32768), dtype=torch.uint8, device="cuda")
     out_d = torch.empty_like(d["q"])
     out_c = torch.empty_like(d["q"])
     out_v = torch.empty_like(vl["q"])
-    out_dec = torch.empty_like(dc["q"])
+    out_dec = torch.empty_like(dc["q"]) if "q" in dc else None
     # Backward inputs: the forward's output and lse (computed once, untimed)
     # and a seeded upstream gradient.
     B_, M_, H_ = d["q"].shape[:3]
@@ -325,7 +425,6 @@ def main():
         ("bwd_noncausal", bwd_item(False)),
         ("bwd_causal", bwd_item(True)),
     ]
-    wanted = set(args.items.split(","))
     unknown = wanted - {n for n, _ in items}
     if unknown:
         print(f"unknown items {sorted(unknown)}", file=sys.stderr)

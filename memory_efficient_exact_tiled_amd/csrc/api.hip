@@ -21,14 +21,29 @@ bool mea_debug() {
 
 bool dtype_ok(int dtype) { return dtype == MEA_FP16 || dtype == MEA_BF16; }
 
-// Compute units of the current device, queried once per device (256 if the
-// query fails). Called only after a call's arguments have been validated.
-// Calls from several host threads may race to fill an entry; they store the
-// same value, and the entries are atomics so that race is well defined.
-int device_compute_units() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+constexpr int kMaxDevices = 64;
+
+// Device a call's work runs on: the device of its stream (the current device
+// for the null stream). -1 if the runtime cannot tell.
+int stream_device(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return -1;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return -1;
+  }
+  return dev;
+}
+
+// Compute units of the device a call's stream runs on, queried once per
+// device (256 if the query fails). Called only after a call's arguments have
+// been validated. Calls from several host threads may race to fill an entry;
+// they store the same value, and the entries are atomics so that race is well
+// defined.
+int device_compute_units(hipStream_t stream) {
+  static std::atomic<int> cached[kMaxDevices];
+  const int dev = stream_device(stream);
+  if (dev < 0 || dev >= kMaxDevices) return 256;
   int cus = cached[dev].load(std::memory_order_relaxed);
   if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
@@ -126,7 +141,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
   bool wide = false;
   if (D == 64 && !causal && block_mask == nullptr) {
     const long long t256 = varlen ? ((long long)M + 255) / 256 + B : ((long long)M + 255) / 256 * B;
-    wide = t256 * Hq >= 2LL * device_compute_units();
+    wide = t256 * Hq >= 2LL * device_compute_units(static_cast<hipStream_t>(stream));
   }
   const int BM = mea::fwd_block_m(D, causal, block_mask != nullptr, wide);
 
@@ -435,7 +450,8 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   p.ws_o = reinterpret_cast<float*>(ws + lay.plan);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.plan + lay.o);
   // Split work-groups: one per compute unit (8 waves fill one).
-  p.grid = device_compute_units() < mea::kDecodeMaxSplit ? device_compute_units() : mea::kDecodeMaxSplit;
+  const int cus = device_compute_units(static_cast<hipStream_t>(stream));
+  p.grid = cus < mea::kDecodeMaxSplit ? cus : mea::kDecodeMaxSplit;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -28,7 +28,9 @@
 //       v_mfma_f32_16x16x32 (row = key, k = head dim), the query heads of the
 //       group form the B operand (one column per head), so S^T = K Q^T reads
 //       each key once for all heads of the group;
-//     * the online softmax runs per head (one head per lane column);
+//     * the online softmax runs per head (one head per lane column); P is
+//       rounded to the input type and the row sum is taken over the rounded
+//       values, so the normaliser matches the weights P.V uses;
 //     * V rows go HBM -> registers -> the wave's LDS region and come back
 //       transposed through ds_read_b64_tr_b16 as the A operand of
 //       O^T = V^T P^T (v_mfma_f32_16x16x16);
@@ -259,15 +261,23 @@ decode_split_kernel(const DecParams p) {
     }
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
     T pv[KB * 4];
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = fast_exp2(s[kb][r] - mu);
-        psum += e;
-        pv[kb * 4 + r] = (T)e;
-      }
+      for (int r = 0; r < 4; ++r) pv[kb * 4 + r] = (T)fast_exp2(s[kb][r] - mu);
+    // Row sum of the rounded P (the weights P.V uses, as in the forward), two
+    // at a time.
+    typedef T T2 __attribute__((ext_vector_type(2)));
+    const T2 one2 = {(T)1.f, (T)1.f};
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < KB * 4; u += 2) {
+      const T2 pp = {pv[u], pv[u + 1]};
+      if constexpr (__is_same(T, __bf16))
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
+      else
+        psum = __builtin_amdgcn_fdot2(pp, one2, psum, false);
+    }
     l_run += psum;
 
     // V block -> this wave's LDS region, then O^T += V^T P^T. LDS operations

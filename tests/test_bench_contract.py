@@ -14,37 +14,62 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
-def _tree(tmp_path, fingerprints):
-    """A copy of the kernel sources under tmp_path with a traffic file whose
-    stored code fingerprints are `fingerprints(name, text)`."""
-    t = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))
-    csrc = tmp_path / "memory_efficient_exact_tiled_amd" / "csrc"
+def _tree(tmp_path, stale=False):
+    """A copy of the sources the traffic guard fingerprints under tmp_path, with
+    a traffic file whose stored fingerprints are those of the copy (or zeros)."""
+    import shutil
+
+    import bench
+    pkg = tmp_path / "memory_efficient_exact_tiled_amd"
+    csrc = pkg / "csrc"
     csrc.mkdir(parents=True)
-    stored = {}
-    for name in t["code_sha256_16"]:
-        text = open(os.path.join(ROOT, "memory_efficient_exact_tiled_amd", "csrc", name)).read()
-        (csrc / name).write_text(text)
-        stored[name] = fingerprints(name, text)
+    for name in bench.TRAFFIC_SOURCES:
+        shutil.copy(os.path.join(ROOT, "memory_efficient_exact_tiled_amd", "csrc", name), csrc / name)
+    shutil.copy(os.path.join(ROOT, "memory_efficient_exact_tiled_amd", "build.py"), pkg / "build.py")
+    fp = bench.code_fingerprints(str(tmp_path))
+    if stale:
+        fp = {k: "0" * 16 for k in fp}
     prof = tmp_path / "profiles"
     prof.mkdir()
-    (prof / "hbm_traffic.json").write_text(json.dumps(dict(t, code_sha256_16=stored)))
-    return csrc
+    t = {"code_sha256_16": fp, "fetch_factor": 2.0, "write_factor": 1.0,
+         "kernels": {"fwd_kernelIDF16bLi64": {"fetch_bytes": 1.0, "write_bytes": 2.0, "dispatches": 1}}}
+    (prof / "hbm_traffic.json").write_text(json.dumps(t))
+    return pkg
 
 
 def test_traffic_is_null_once_a_kernel_changes(tmp_path, monkeypatch):
     import bench
-    _tree(tmp_path, lambda name, text: "0" * 16)
+    _tree(tmp_path, stale=True)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic() is None
 
 
 def test_traffic_survives_comment_edits_but_not_code_edits(tmp_path, monkeypatch):
     import bench
-    csrc = _tree(tmp_path, lambda name, text: bench.kernel_code_hash(text))
+    pkg = _tree(tmp_path)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic() is not None
-    fwd = csrc / "fwd.hip"
+    fwd = pkg / "csrc" / "fwd.hip"
     fwd.write_text("// a new comment line\n\n/* and a block\n   comment */\n" + fwd.read_text().replace("\n", "  // note\n", 3))
     assert bench.measured_traffic() is not None
     fwd.write_text(fwd.read_text() + "\nstatic const int kAnotherConstant = 1;\n")
     assert bench.measured_traffic() is None
+
+
+def test_traffic_is_null_after_a_host_side_or_flag_change(tmp_path, monkeypatch):
+    """Kernel choice and tile height are made on the host (api.hip), launch
+    parameters live in launch.hpp, and the code depends on the compiler flags."""
+    import bench
+    for target, edit in (("csrc/api.hip", lambda t: t + "\nstatic const int kTileChoice = 3;\n"),
+                         ("csrc/launch.hpp", lambda t: t.replace("kDecodeMaxSplit = 1024", "kDecodeMaxSplit = 512")),
+                         ("build.py", lambda t: t.replace('"-O3",', '"-O2",'))):
+        sub = tmp_path / target.replace("/", "_").replace(".", "_")
+        sub.mkdir()
+        pkg = _tree(sub)
+        monkeypatch.setattr(bench, "ROOT", str(sub))
+        assert bench.measured_traffic() is not None, target
+        f = pkg / target
+        new = edit(f.read_text())
+        assert new != f.read_text(), target
+        f.write_text(new)
+        assert bench.measured_traffic() is None, target

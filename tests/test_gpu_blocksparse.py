@@ -132,7 +132,7 @@ def test_blocksparse_bwd_parity(mea, case):
     """Backward over a block-sparse mask (mea_bwd_blocksparse) against the
     oracle, with the backward tests' tolerance; one query block and one key
     block are fully off (their dq, resp. dk and dv, are exactly 0)."""
-    from test_gpu_bwd import C, U
+    from grad_bounds import check_grads, grad_terms
     name, seed, B, M, N, Hq, Hkv, D, dt, causal, alibi, dens = case
     say(f"case blocksparse {name}")
     c = inp.dense_case(seed, B, M, N, Hq, Hkv, D, dt)
@@ -150,10 +150,9 @@ def test_blocksparse_bwd_parity(mea, case):
     got = mea.bwd(q, k, v, out, dod, lse, causal=causal, scale=scale, alibi_slopes=sl, block_mask=m)
     torch.cuda.synchronize()
     want = orc.bwd(c["q"], c["k"], c["v"], do, dt, scale, causal=causal, alibi_slopes=slopes, block_mask=bm)
-    for label, g, w in zip(("dq", "dk", "dv"), got, want):
-        gh = host_f64(g)
-        tol = C * U[dt] * float(np.max(np.abs(w)))
-        assert report(f"{name} {label}", gh, w, tol) <= tol, label
+    terms = grad_terms(c["q"], c["k"], c["v"], do, dt, scale, causal=causal, alibi_slopes=slopes,
+                       block_mask=bm)[1]
+    check_grads(name, [host_f64(g) for g in got], want, terms, dt, say=say)
     assert np.all(host_f64(got[0])[:, 64:128] == 0), "dq of a query block with every block off"
     assert np.all(host_f64(got[1])[:, 128:192] == 0) and np.all(host_f64(got[2])[:, 128:192] == 0), \
         "dk, dv of a key block no query sees"

@@ -13,10 +13,10 @@ import torch
 import mea_inputs as inp
 import oracle.attention as orc
 from gpu_util import LSE_TOL, TOL, dev, f32, host_f64, i32, say
+from grad_bounds import check_grads, grad_terms
 
 pytestmark = pytest.mark.gpu
 
-U = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 SEEDS = range(16)
 
 
@@ -85,10 +85,9 @@ def test_random_blocksparse_fwd_bwd(mea, seed):
     assert float(np.max(np.abs(host_f64(out) - want), initial=0.0)) <= TOL[dt], "out"
     _check_lse(lse.cpu().numpy(), wlse, dt)
     wg = orc.bwd(c["q"], c["k"], c["v"], do, dt, scale, causal=causal, alibi_slopes=slopes, block_mask=bm)
-    for name, g, w in zip(("dq", "dk", "dv"), grads, wg):
-        ref = float(np.max(np.abs(w), initial=0.0))
-        err = float(np.max(np.abs(host_f64(g) - w), initial=0.0))
-        assert err <= 4 * U[dt] * ref + 1e-5, (name, err, ref)
+    terms = grad_terms(c["q"], c["k"], c["v"], do, dt, scale, causal=causal, alibi_slopes=slopes,
+                       block_mask=bm)[1]
+    check_grads(f"random blocksparse {seed}", [host_f64(g) for g in grads], wg, terms, dt, say=say)
 
 
 @pytest.mark.parametrize("seed", SEEDS)

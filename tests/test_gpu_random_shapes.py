@@ -12,10 +12,10 @@ import torch
 import mea_inputs as inp
 import oracle.attention as orc
 from gpu_util import LSE_TOL, TOL, dev, f32, host_f64, i32, say
+from grad_bounds import check_grads, grad_terms
 
 pytestmark = pytest.mark.gpu
 
-U = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
 def _draw(seed):
@@ -80,9 +80,8 @@ def test_random_shape(mea, seed):
     assert np.max(np.abs(gl[fin] - wl[fin]), initial=0.0) <= LSE_TOL[dt], "lse"
 
     wg = orc.bwd(c["q"], c["k"], c["v"], do, dt, scale, causal=cfg["causal"], alibi_slopes=slopes, **kw_orc)
-    for name, g, w in zip(("dq", "dk", "dv"), grads, wg):
-        ref = float(np.max(np.abs(w), initial=0.0))
-        err = float(np.max(np.abs(host_f64(g) - w), initial=0.0))
-        # the backward tests' bound (4 u max|grad|), with the fp32 floor of
-        # gradients that vanish exactly (one allowed key: dq = dk = 0)
-        assert err <= 4 * U[dt] * ref + 1e-5, (name, err, ref)
+    # the backward tests' element-wise bar (C u times the magnitude sum of each
+    # element's own terms)
+    terms = grad_terms(c["q"], c["k"], c["v"], do, dt, scale, causal=cfg["causal"], alibi_slopes=slopes,
+                       **kw_orc)[1]
+    check_grads(f"random {seed}", [host_f64(g) for g in grads], wg, terms, dt, say=say)
