@@ -37,6 +37,7 @@ extern "C" {
 #define MEA_EUNSUPPORTED 2 /* (dtype, head dim) combination without a kernel */
 #define MEA_EWORKSPACE 3   /* workspace missing, too small or not 256-byte aligned */
 #define MEA_EHIP 4         /* the HIP runtime rejected a launch */
+#define MEA_ESCRATCH 5     /* mea_decode_noalloc: the step needs more than its static scratch */
 
 /* Element types of q, k, v, caches and outputs. */
 #define MEA_FP16 0
@@ -242,6 +243,31 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
                void* out, int B, int Hq, int Hkv, int D, int S_max, float scale,
                const float* alibi_slopes, int dtype,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mea_decode_noalloc - mea_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same step, the same kernels and the same results
+ * as mea_decode, with the workspace taken from a static device array of
+ * MEA_DECODE_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * device it runs on until the process ends. The call allocates and frees
+ * nothing. Arguments and errors as mea_decode, without the workspace.
+ *
+ * Limit: the step needs P + O + L bytes of scratch, P = (B + 2) * 4 rounded
+ * up to 256, O = (G + B) * Hq * D * 4 rounded up to 256, L = (G + B) * Hq * 8,
+ * with G the compute units of the stream's device (256 on MI355X); a larger
+ * step returns MEA_ESCRATCH and launches nothing. (B=32, Hq=32, D=128 needs
+ * 4.8 MB.)
+ * The scratch is shared by every call on a device and keeps the last call's
+ * contents (each call writes every byte it reads before reading it): calls
+ * on one device whose work may overlap in time (different streams, or
+ * different host threads without ordering) race on it and must be
+ * serialised by the caller.
+ */
+#define MEA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mea_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens,
+                       void* out, int B, int Hq, int Hkv, int D, int S_max, float scale,
+                       const float* alibi_slopes, int dtype, void* stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* mea_strerror(int status);

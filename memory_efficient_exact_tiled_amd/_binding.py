@@ -19,12 +19,13 @@ import torch  # noqa: F401
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmea.so")
 
-MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP = 0, 1, 2, 3, 4
+MEA_OK, MEA_EINVAL, MEA_EUNSUPPORTED, MEA_EWORKSPACE, MEA_EHIP, MEA_ESCRATCH = 0, 1, 2, 3, 4, 5
+MEA_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/mea.h
 MEA_FP16, MEA_BF16 = 0, 1
 MEA_MASK_CAUSAL, MEA_MASK_BLOCKDIAG, MEA_BIAS_ALIBI = 1, 2, 4
 
 EXPORTS = ("mea_fwd", "mea_fwd_blocksparse", "mea_block_sparse_block", "mea_bwd", "mea_bwd_blocksparse", "mea_bwd_workspace_bytes", "mea_fwd_kvcache", "mea_kv_append", "mea_decode",
-           "mea_decode_workspace_bytes", "mea_strerror", "mea_supported", "mea_decode_chunk")
+           "mea_decode_noalloc", "mea_decode_workspace_bytes", "mea_strerror", "mea_supported", "mea_decode_chunk")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python memory_efficient_exact_tiled_amd/build.py`")
@@ -51,6 +52,8 @@ _lib.mea_kv_append.restype = _i
 _lib.mea_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
 _lib.mea_decode.restype = _i
 _lib.mea_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _vp]
+_lib.mea_decode_noalloc.restype = _i
+_lib.mea_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp]
 _lib.mea_decode_workspace_bytes.restype = _sz
 _lib.mea_decode_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.mea_strerror.restype = ctypes.c_char_p
@@ -288,6 +291,29 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, alibi_slo
     _check(_lib.mea_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(ctx_lens), _ptr(out), B, Hq, Hkv, D, S_max,
                            float(scale), _ptr(alibi_slopes), _dtype_code(q), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_noalloc(q, kcache, vcache, ctx_lens, out, *, scale: float | None = None, alibi_slopes=None,
+                   stream=None):
+    """``mea_decode_noalloc``: the decode step of :func:`decode` with the
+    library's static per-device scratch instead of a workspace. ``out``
+    ``[B,Hq,D]`` is required (this call allocates nothing). Calls that may
+    overlap on one device race on the scratch."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Bc, S_max, Hkv, Dc = kcache.shape
+    if Bc != B or Dc != D or vcache.shape != kcache.shape:
+        raise ValueError("q and cache shapes disagree")
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype or out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("q, caches and out must share a dtype; out is shaped like q")
+    if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
+        raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_cuda(q, kcache, vcache, ctx_lens, out, alibi_slopes)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(_lib.mea_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(ctx_lens), _ptr(out), B, Hq, Hkv, D,
+                                   S_max, float(scale), _ptr(alibi_slopes), _dtype_code(q), _stream(stream)))
     return out
 
 

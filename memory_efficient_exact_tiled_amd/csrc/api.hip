@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mea.h"
 #include "launch.hpp"
@@ -96,6 +97,7 @@ const char* mea_strerror(int status) {
     case MEA_EUNSUPPORTED: return "unsupported dtype or head dimension";
     case MEA_EWORKSPACE: return "workspace missing, too small or misaligned";
     case MEA_EHIP: return "HIP runtime error";
+    case MEA_ESCRATCH: return "problem too large for the library's static decode scratch (mea_decode_noalloc)";
     default: return "unknown status";
   }
 }
@@ -389,18 +391,20 @@ namespace {
 
 // Decode workspace: the plan ([B + 2] int32: prefix sums of ctx, then the span
 // of keys per split work-group), then the partial outputs [R][Hq][D] and the
-// (max, sum) pairs [R][Hq][2], R = kDecodeMaxSplit + B rows, each part
-// 256-byte aligned. Split work-group w writes its partial of sequence b to row
-// w + b: the sequences of a work-group are consecutive and so are the
-// work-groups of a sequence, so w + b is unique and below G + B for
-// G <= kDecodeMaxSplit work-groups, whatever S_max is.
+// (max, sum) pairs [R][Hq][2], R = G_max + B rows, each part 256-byte
+// aligned. Split work-group w writes its partial of sequence b to row w + b:
+// the sequences of a work-group are consecutive and so are the work-groups of
+// a sequence, so w + b is unique and below G + B for G <= G_max split
+// work-groups, whatever S_max is. A caller's workspace is sized for G_max =
+// kDecodeMaxSplit (any device); the static scratch of mea_decode_noalloc for
+// the split work-groups of the device it runs on.
 struct DecLayout {
   size_t plan, o, ml, total;
 };
 
-DecLayout dec_layout(int B, int Hq, int D) {
+DecLayout dec_layout(int B, int Hq, int D, int max_split) {
   DecLayout l{};
-  const size_t rows = (size_t)mea::kDecodeMaxSplit + (size_t)B;
+  const size_t rows = (size_t)max_split + (size_t)B;
   const size_t slots = rows * (size_t)Hq;
   l.plan = ((size_t)(B + 2) * sizeof(int32_t) + 255) & ~(size_t)255;
   l.o = (slots * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
@@ -409,18 +413,9 @@ DecLayout dec_layout(int B, int Hq, int D) {
   return l;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {
-  if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
-  return dec_layout(B, Hq, D).total;
-}
-
-int mea_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
-               int Hq, int Hkv, int D, int S_max, float scale, const float* alibi_slopes, int dtype,
-               void* workspace, size_t workspace_bytes, void* stream) {
+// Host-side checks shared by mea_decode and mea_decode_noalloc.
+int decode_check(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, const void* out,
+                 int B, int Hq, int Hkv, int D, int S_max, float scale, int dtype) {
   if (q == nullptr || kcache == nullptr || vcache == nullptr || ctx_lens == nullptr || out == nullptr)
     return MEA_EINVAL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || S_max <= 0) return MEA_EINVAL;
@@ -430,14 +425,15 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   if ((long long)Hkv * D > 0x7fffffffLL) return MEA_EINVAL;
   // Context prefix sums are int32 on the device.
   if ((long long)B * (long long)S_max > 0x7fffffffLL) return MEA_EINVAL;
-  const size_t need = mea_decode_workspace_bytes(B, Hq, D, S_max);
-  if (workspace == nullptr || workspace_bytes < need) return MEA_EWORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return MEA_EWORKSPACE;
-  const DecLayout lay = dec_layout(B, Hq, D);
-  const int group = Hq / Hkv;
-  const int nhb = (group + 15) / 16;
+  const int nhb = (Hq / Hkv + 15) / 16;
   if ((long long)Hkv * nhb > 65535 || B > 65535) return MEA_EINVAL;
+  return MEA_OK;
+}
 
+// Fills DecParams over the workspace ws (laid out by lay) and launches.
+int decode_launch(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
+                  int Hq, int Hkv, int D, int S_max, float scale, const float* alibi_slopes, int dtype, char* ws,
+                  const DecLayout& lay, int grid, hipStream_t st) {
   mea::DecParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.kc = static_cast<const uint16_t*>(kcache);
@@ -445,28 +441,94 @@ int mea_decode(const void* q, const void* kcache, const void* vcache, const int3
   p.ctx = ctx_lens;
   p.out = static_cast<uint16_t*>(out);
   p.slopes = alibi_slopes;
-  char* ws = static_cast<char*>(workspace);
   p.plan = reinterpret_cast<int*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + lay.plan);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.plan + lay.o);
-  // Split work-groups: one per compute unit (8 waves fill one).
-  const int cus = device_compute_units(static_cast<hipStream_t>(stream));
-  p.grid = cus < mea::kDecodeMaxSplit ? cus : mea::kDecodeMaxSplit;
+  p.grid = grid;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
-  p.group = group;
+  p.group = Hq / Hkv;
   p.S_max = S_max;
-  p.nhb = nhb;
+  p.nhb = (p.group + 15) / 16;
   p.alibi = alibi_slopes != nullptr;
   p.scale_log2 = scale * 1.4426950408889634f;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (mea_debug()) {
     const int rc = debug_check_ctx(ctx_lens, B, S_max, st);
     if (rc != MEA_OK) return rc;
   }
   return mea::launch_decode(dtype, D, p, st) == hipSuccess ? MEA_OK : MEA_EHIP;
+}
+
+// Split work-groups of a decode step: one per compute unit of the stream's
+// device (8 waves fill one), at most kDecodeMaxSplit.
+int decode_grid(hipStream_t st) {
+  const int cus = device_compute_units(st);
+  return cus < mea::kDecodeMaxSplit ? cus : mea::kDecodeMaxSplit;
+}
+
+// Scratch of mea_decode_noalloc: the decode workspace in a static device
+// array, one copy per device the library runs on, kept until the process
+// ends. Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[MEA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+char* scratch_ptr(int dev) {
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = ptrs[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return static_cast<char*>(ptr);
+  std::lock_guard<std::mutex> lock(mu);
+  ptr = ptrs[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return static_cast<char*>(ptr);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* found = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&found, HIP_SYMBOL(scratch));
+  if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+  if (e != hipSuccess || found == nullptr) return nullptr;
+  ptrs[dev].store(found, std::memory_order_release);
+  return static_cast<char*>(found);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mea_decode_workspace_bytes(int B, int Hq, int D, int S_max) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
+  return dec_layout(B, Hq, D, mea::kDecodeMaxSplit).total;
+}
+
+int mea_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
+               int Hq, int Hkv, int D, int S_max, float scale, const float* alibi_slopes, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = decode_check(q, kcache, vcache, ctx_lens, out, B, Hq, Hkv, D, S_max, scale, dtype);
+  if (rc != MEA_OK) return rc;
+  const DecLayout lay = dec_layout(B, Hq, D, mea::kDecodeMaxSplit);
+  if (workspace == nullptr || workspace_bytes < lay.total) return MEA_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return MEA_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return decode_launch(q, kcache, vcache, ctx_lens, out, B, Hq, Hkv, D, S_max, scale, alibi_slopes, dtype,
+                       static_cast<char*>(workspace), lay, decode_grid(st), st);
+}
+
+int mea_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out,
+                       int B, int Hq, int Hkv, int D, int S_max, float scale, const float* alibi_slopes, int dtype,
+                       void* stream) {
+  const int rc = decode_check(q, kcache, vcache, ctx_lens, out, B, Hq, Hkv, D, S_max, scale, dtype);
+  if (rc != MEA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int grid = decode_grid(st);
+  const DecLayout lay = dec_layout(B, Hq, D, grid);
+  if (lay.total > (size_t)MEA_DECODE_NOALLOC_SCRATCH_BYTES) return MEA_ESCRATCH;
+  char* ws = scratch_ptr(stream_device(st));
+  if (ws == nullptr) return MEA_EHIP;
+  return decode_launch(q, kcache, vcache, ctx_lens, out, B, Hq, Hkv, D, S_max, scale, alibi_slopes, dtype, ws, lay,
+                       grid, st);
 }
 
 }  // extern "C"

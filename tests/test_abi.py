@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_strerror_and_supported():
     assert mea.strerror(0) == "success"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert mea.strerror(s) and mea.strerror(s) != "unknown status"
     assert mea.strerror(99) == "unknown status"
     for dt in (mea.MEA_FP16, mea.MEA_BF16):
@@ -105,6 +105,32 @@ def _dec(**kw):
 ])
 def test_decode_rejects(kw, status):
     assert _dec(**kw) == status
+
+
+def _dec_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ctx=FAKE, out=FAKE, B=2, Hq=4, Hkv=2, D=128, S=1024, scale=0.1, sl=None,
+             dtype=mea.MEA_FP16, stream=None)
+    a.update(kw)
+    return mea.lib().mea_decode_noalloc(a["q"], a["kc"], a["vc"], a["ctx"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                        a["D"], a["S"], a["scale"], a["sl"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ctx=None), mea.MEA_EINVAL),
+    (dict(out=None), mea.MEA_EINVAL),
+    (dict(B=0), mea.MEA_EINVAL),
+    (dict(Hq=6, Hkv=4), mea.MEA_EINVAL),
+    (dict(scale=float("nan")), mea.MEA_EINVAL),
+    (dict(D=32), mea.MEA_EUNSUPPORTED),
+    (dict(B=4, S=1 << 29), mea.MEA_EINVAL),
+    # (256 + 4096) * 64 * (128 + 2) * 4 bytes of partials: more than the scratch
+    (dict(B=4096, Hq=64, Hkv=8, S=8), mea.MEA_ESCRATCH),
+])
+def test_decode_noalloc_rejects(kw, status):
+    """Refused on the host before any HIP call, including a step larger than
+    the static scratch (MEA_DECODE_NOALLOC_SCRATCH_BYTES)."""
+    assert _dec_noalloc(**kw) == status
+    assert "scratch" in mea.strerror(mea.MEA_ESCRATCH)
 
 
 def _bwd(**kw):
