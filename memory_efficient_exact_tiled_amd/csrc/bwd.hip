@@ -101,23 +101,6 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
   }
 }
 
-// Segment of a packed batch holding logical tile t, with tiles of `bt` rows
-// counted over the boundaries in `st` (clamped to [0, total]). Returns the
-// segment index (B if t is past the last tile) and the tile's rank in it.
-__device__ __forceinline__ int find_tile(const int32_t* st, int B, int total, int bt, int t, int& rank, int& a0,
-                                         int& a1, int& ntile) {
-  int acc = 0, s = 0;
-  for (; s < B; ++s) {
-    a0 = min(max(st[s], 0), total);
-    a1 = min(max(st[s + 1], a0), total);
-    ntile = (a1 - a0 + bt - 1) / bt;
-    if (t < acc + ntile) break;
-    acc += ntile;
-  }
-  rank = t - acc;
-  return s;
-}
-
 // ---- dQ ------------------------------------------------------------------------
 template <typename T, int D, int CS, int AL, int BS = 0>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWpe<D>, kBwdWpe<D>))) bwd_dq_kernel(const BwdParams p) {
@@ -147,8 +130,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   if (CS == 1) {
     if (pid >= p.total_wg_q) return;
     const int nbh = p.varlen ? p.Hq : p.B * p.Hq;
-    t = pid / nbh;
-    bh = pid - t * nbh;
+    causal_order(pid, nbh, p.group, t, bh);
   } else {
     const int lid = (pid & 7) * p.wg_per_xcd_q + (pid >> 3);
     if (lid >= p.total_wg_q) return;
@@ -170,7 +152,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     st_off = ((long long)b * p.Hq + h) * p.M;
   } else {
     int rank, a0 = 0, a1 = 0, ntile = 0;
-    const int s = find_tile(p.seqstart_q, p.B, p.M, BM, t, rank, a0, a1, ntile);
+    const int s = find_segment_tile(p.seqstart_q, p.B, p.M, BM, t, rank, a0, a1, ntile);
     if (s >= p.B) return;
     tile = CAUSAL ? (ntile - 1 - rank) : rank;
     const int k0 = min(max(p.seqstart_k[s], 0), p.N);
@@ -434,8 +416,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
   if (CS == 1) {
     if (pid >= p.total_wg_k) return;
     const int nbg = p.varlen ? p.Hkv : p.B * p.Hkv;
-    t = pid / nbg;
-    bg = pid - t * nbg;
+    causal_order(pid, nbg, 1, t, bg);
   } else {
     const int lid = (pid & 7) * p.wg_per_xcd_k + (pid >> 3);
     if (lid >= p.total_wg_k) return;
@@ -456,7 +437,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWp
     st_base = (long long)b * p.Hq * p.M;
   } else {
     int rank, a0 = 0, a1 = 0, ntile = 0;
-    const int s = find_tile(p.seqstart_k, p.B, p.N, BNK, t, rank, a0, a1, ntile);
+    const int s = find_segment_tile(p.seqstart_k, p.B, p.N, BNK, t, rank, a0, a1, ntile);
     if (s >= p.B) return;
     tile = rank;
     const int q0 = min(max(p.seqstart_q[s], 0), p.M);

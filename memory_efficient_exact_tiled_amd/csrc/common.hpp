@@ -161,6 +161,57 @@ struct TileSkipList {
   }
 };
 
+// Packed batches: segment s of the prefix sums st (clamped to [0, total])
+// owns the logical tiles [base(s), base(s) + ntile(s)) of height bt, with
+// base(s) = floor(st[s] / bt) + s and ntile(s) = ceil(len(s) / bt). Since
+// floor(st[s+1] / bt) - floor(st[s] / bt) + 1 >= ceil(len(s) / bt), these
+// ranges are disjoint and in segment order, and they end at or before
+// ceil(total / bt) + B. The segment of logical tile t is then the last s with
+// base(s) <= t, found by binary search: O(log B) reads of st whatever the
+// number of segments (a serial scan costs O(B) per work-group). Returns that
+// segment and the tile's rank in it, or B when t falls in the gap after a
+// segment's last tile (that work-group has nothing to do). Malformed prefix
+// sums give wrong segments but every returned row range stays in [0, total].
+__device__ __forceinline__ int find_segment_tile(const int32_t* st, int B, int total, int bt, int t, int& rank,
+                                                 int& a0, int& a1, int& ntile) {
+  auto base = [&](int s) { return min(max(st[s], 0), total) / bt + s; };
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base(mid) <= t) lo = mid; else hi = mid - 1;
+  }
+  const int b0 = base(lo);
+  a0 = min(max(st[lo], 0), total);
+  a1 = min(max(st[lo + 1], a0), total);
+  ntile = (a1 - a0 + bt - 1) / bt;
+  rank = t - b0;
+  return (rank >= 0 && rank < ntile) ? lo : B;
+}
+
+// Launch order of causal launches: logical work-group pid -> (tile rank t,
+// head slot bh), tile rank major (longest tiles first) with the head slots
+// innermost. A head slot is bh = stream * group + r, where a stream is one
+// (batch row, KV head) whose group query heads read the same K/V. Work-group
+// p runs on XCD p % 8, and every XCD has its own L2: when the streams split
+// evenly over the 8 XCDs, stream s is pinned to XCD s % 8, so all query heads
+// reading one K/V stream share one L2 (each K/V byte is then fetched from HBM
+// once, not once per XCD its query heads were dealt to). Otherwise the head
+// slots are dealt round-robin over the XCDs.
+__host__ __device__ inline void causal_order(int pid, int nbh, int group, int& t, int& bh) {
+  const int nstreams = nbh / group;
+  if ((nstreams & 7) != 0 || group == 1) {
+    t = pid / nbh;                       // with group == 1 this is the same pinning
+    bh = pid - t * nbh;
+    return;
+  }
+  const int x = pid & 7;
+  const int hpx = nbh >> 3;              // head slots per XCD per tile rank
+  const int slot = pid >> 3;
+  t = slot / hpx;
+  const int rem = slot - t * hpx;
+  bh = (x + 8 * (rem / group)) * group + rem % group;
+}
+
 // 2^x on the transcendental unit (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -152,6 +152,19 @@ def test_bwd_vanishing_dq_dk(mea, case):
     _check(name, (dq, dk, dv), want, terms, dt)
 
 
+def test_varlen_bwd_thousands_of_short_segments(mea):
+    """4096 packed segments of 1 to 64 tokens (some empty), causal with GQA:
+    both backward kernels find their segment by binary search (query tiles
+    over seqstart_q, key tiles over seqstart_k)."""
+    lengths = [int(x) for x in np.random.default_rng(13).integers(0, 65, 4096)]
+    c = inp.varlen_case(14, lengths, 4, 2, 64, "bf16")
+    say(f"case bwd packed 4096 short segments, T={int(c['seqstart'][-1])}")
+    do = inp.normal_bits(514, c["q"].shape, "bf16", 0)
+    got, scale = _fwd_bwd(mea, c["q"], c["k"], c["v"], do, "bf16", causal=True, st=c["seqstart"])
+    want, terms = _want(c["q"], c["k"], c["v"], do, "bf16", scale, causal=True, seqstart_q=c["seqstart"])
+    _check("bwd 4096 short segments", got, want, terms, "bf16")
+
+
 def test_varlen_bwd_equals_per_segment_bitwise(mea):
     """Tiles start at segment starts, so the packed backward of each segment
     is the same arithmetic as that segment run alone: bitwise equal."""

@@ -138,15 +138,51 @@ def test_varlen_gqa_alibi_full_config(mea):
         assert report(f"cfg4 seg{s} L={L}", got[0, st[s] + rows], want, TOL["bf16"]) <= TOL["bf16"]
 
 
+def test_varlen_thousands_of_short_segments(mea):
+    """4096 packed segments of 1 to 64 tokens (some empty), causal + ALiBi with
+    GQA: every work-group finds its segment by a binary search over the
+    segments' tile ranges. Whole output and lse against the oracle; the
+    launch is timed on its own."""
+    lengths = [int(x) for x in np.random.default_rng(11).integers(0, 65, 4096)]
+    dt, Hq, Hkv, D = "bf16", 8, 2, 64
+    c = inp.varlen_case(12, lengths, Hq, Hkv, D, dt)
+    T = int(c["seqstart"][-1])
+    say(f"case packed 4096 short segments, T={T}")
+    slopes = inp.alibi_slopes(Hq)
+    q, k, v = dev(c["q"], dt), dev(c["k"], dt), dev(c["v"], dt)
+    st, sl = i32(c["seqstart"]), f32(slopes)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    lse = torch.full((Hq, T), 7.0, dtype=torch.float32, device="cuda")
+    out = mea.fwd(q, k, v, causal=True, scale=scale, seqstart_q=st, alibi_slopes=sl, lse=lse)
+    torch.cuda.synchronize()
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=True, seqstart_q=c["seqstart"],
+                         alibi_slopes=slopes)
+    assert report("4096 short segments", host_f64(out), want, TOL[dt]) <= TOL[dt]
+    fin = np.isfinite(wlse[0])
+    got_lse = lse.cpu().numpy()
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    assert np.max(np.abs(got_lse[fin] - wlse[0][fin])) <= LSE_TOL[dt]
+    for _ in range(3):
+        mea.fwd(q, k, v, causal=True, scale=scale, seqstart_q=st, alibi_slopes=sl, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        mea.fwd(q, k, v, causal=True, scale=scale, seqstart_q=st, alibi_slopes=sl, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    say(f"4096 short segments (T={T}, Hq=8, D=64, causal ALiBi): {e0.elapsed_time(e1) / 20 * 1e3:.1f} us per launch")
+
+
 VARLEN = [
     # name, lengths, Hq, Hkv, D, dtype, causal, alibi
     ("ragged_segments_causal_alibi_d128", [1, 63, 64, 65, 130, 7, 256, 257], 8, 2, 128, "bf16", True, True),
     ("ragged_segments_noncausal_d64_fp16", [5, 300, 1, 129], 4, 4, 64, "fp16", False, False),
     ("ragged_segments_noncausal_alibi", [40, 100, 3], 4, 1, 64, "bf16", False, True),
     ("one_segment", [513], 2, 1, 128, "fp16", True, False),
-    # the launch order of packed batches: one segment per lane up to 64
-    # segments (exactly 64 here, some empty), a serial scan beyond (70), and
-    # the head split across XCDs only when Hq is a multiple of 8 (6 here)
+    # packed batches: work-groups find their segment by a binary search over
+    # the segments' tile ranges (64 and 70 segments, some empty, cover odd and
+    # even search depths), and the causal launch order pins each KV head to
+    # one XCD only when the KV heads split evenly over the 8 XCDs (not for Hq=6)
     ("segments_64_causal_hq8", [0, 3] + [int(x) for x in np.random.default_rng(5).integers(1, 150, 61)] + [0],
      8, 2, 64, "bf16", True, False),
     ("segments_70_causal_alibi", [int(x) for x in np.random.default_rng(6).integers(0, 120, 70)],
