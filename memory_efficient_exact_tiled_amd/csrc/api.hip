@@ -134,7 +134,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
   const long long q_rstride = (long long)Hq * D, kv_rstride = (long long)Hkv * D;
   if (q_rstride > 0x7fffffffLL || kv_rstride > 0x7fffffffLL) return MEA_EINVAL;
   if (block_mask != nullptr && (varlen || kv_lens != nullptr)) return MEA_EINVAL;
-  // Work-group counts are int32; checked here at the smallest tile height.
+  // Work-group counts are int32; checked here at the smallest tile height
+  // (128 rows of one head, or 32 rows of 4 heads), and exactly below.
   const long long t128 = varlen ? ((long long)M + 127) / 128 + B : ((long long)M + 127) / 128 * B;
   if (t128 * Hq > 0x7fffffffLL - 8) return MEA_EINVAL;
   // Dense D=64 without mask takes 256-row work-groups when there are enough
@@ -145,7 +146,10 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
     const long long t256 = varlen ? ((long long)M + 255) / 256 + B : ((long long)M + 255) / 256 * B;
     wide = t256 * Hq >= 2LL * device_compute_units(static_cast<hipStream_t>(stream));
   }
-  const int BM = mea::fwd_block_m(D, causal, block_mask != nullptr, wide);
+  // Causal launches whose KV heads serve a multiple of 4 query heads use
+  // 32-row work-groups of 4 query heads (one per wave) sharing one KV head.
+  const bool gq = causal && block_mask == nullptr && (Hq / Hkv) % 4 == 0;
+  const int BM = mea::fwd_block_m(D, causal, block_mask != nullptr, wide, gq);
 
   mea::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -169,18 +173,19 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, int B, int 
   p.varlen = varlen;
   p.alibi = alibi;
   p.wide = wide;
+  p.gq = gq;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.q_rstride = (int)q_rstride;
   p.kv_rstride = (int)kv_rstride;
   long long tiles, total;
   if (varlen) {
     tiles = ((long long)M + BM - 1) / BM + B;   // each segment wastes at most one partial tile
-    total = tiles * Hq;
+    total = tiles * (gq ? Hq / 4 : Hq);
     p.q_bstride = 0;
     p.kv_bstride = 0;
   } else {
     tiles = ((long long)M + BM - 1) / BM;
-    total = tiles * Hq * (long long)B;
+    total = tiles * (gq ? Hq / 4 : Hq) * (long long)B;
     p.q_bstride = (long long)M * q_rstride;
     p.kv_bstride = (long long)N * kv_rstride;
   }

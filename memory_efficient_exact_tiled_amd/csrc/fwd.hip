@@ -79,11 +79,13 @@ constexpr int kBN = 64;
 // from LDS feeds two query blocks); under a causal mask and at D=128 QB=1,
 // which halves the rows a diagonal block masks off and keeps a wave within
 // the register budget of several waves per SIMD.
-template <int D, int QB_>
+template <int D, int QB_, int GQ = 0>
 struct FwdShape {
   static constexpr int QB = QB_;
   static constexpr int QW = 32 * QB;            // query rows per wave
-  static constexpr int BM = kWaves * QW;        // query rows per work-group
+  // Query rows per work-group: GQ = 1 (grouped-query work-groups) gives the
+  // four waves the same rows of four query heads sharing one KV head.
+  static constexpr int BM = GQ ? QW : kWaves * QW;
   // Padded LDS row strides (elements). K rows are read 16 rows x 16 bytes at
   // a time: a stride of 4 banks mod 64 keeps those 16 rows on distinct banks.
   // The transpose read of V covers 4 rows x 2 chunks of 32 bytes per 32
@@ -104,11 +106,15 @@ struct FwdShape {
 // (compile-time constants), 2 = read from p at run time. Causal launches
 // specialise both; the dense launch reads both at run time, which the
 // compiler schedules better than the fully specialised form. BS = 1 reads a
-// block-sparse mask (p.block_mask).
-template <typename T, int D, int QB_, int CS, int AL, int BS = 0>
+// block-sparse mask (p.block_mask). GQ = 1 (causal launches whose KV heads
+// serve a multiple of 4 query heads): a work-group takes 32 query rows of 4
+// query heads that share one KV head, one head per wave, so its waves stop at
+// the same diagonal and one LDS copy of each K/V block serves 4 heads.
+template <typename T, int D, int QB_, int CS, int AL, int BS = 0, int GQ = 0>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE))) fwd_kernel(const FwdParams p) {
-  using S = FwdShape<D, QB_>;
+  using S = FwdShape<D, QB_, GQ>;
+  static_assert(!GQ || (CS == 1 && BS == 0 && QB_ == 1), "grouped-query work-groups are causal, QB = 1");
   using MF = Mfma<T>;
   const bool ALIBI = AL == 2 ? (p.alibi != 0) : AL == 1;
   const bool CAUSAL = CS == 2 ? (p.causal != 0) : CS == 1;
@@ -139,16 +145,19 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
     // second-longest one. Packed: segment by segment, each segment's tiles
     // longest first, for all heads at once.
     if (pid >= p.total_wg) return;
-    const int nbh = p.varlen ? p.Hq : p.B * p.Hq;
-    causal_order(pid, nbh, p.group, t, bh);
+    const int nbh = (p.varlen ? p.Hq : p.B * p.Hq) / (GQ ? kWaves : 1);
+    causal_order(pid, nbh, GQ ? p.group / kWaves : p.group, t, bh);
   } else {
     const int lid = (pid & 7) * p.wg_per_xcd + (pid >> 3);
     if (lid >= p.total_wg) return;
     bh = lid / p.n_qtiles;
     t = lid - bh * p.n_qtiles;
   }
-  const int h = bh % p.Hq;
-  const int b = bh / p.Hq;
+  // GQ: bh counts groups of 4 consecutive query heads (one KV head's, since
+  // the group size is a multiple of 4); wave w takes the w-th of them.
+  const int hq = GQ ? p.Hq / kWaves : p.Hq;
+  const int h = GQ ? (bh % hq) * kWaves + wave : bh % p.Hq;
+  const int b = bh / hq;
   const int g = h / p.group;
 
   int M_s, N_s, tile;
@@ -184,7 +193,7 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   kend = max(kend, 0);
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  const int wq0 = i0 + wave * QW;      // first query row of this wave
+  const int wq0 = i0 + (GQ ? 0 : wave * QW);   // first query row of this wave
   const int wlast = min(wq0 + QW, M_s) - 1;
   int wkend = 0;                       // keys this wave needs
   if (wlast >= wq0) wkend = CAUSAL ? max(min(N_s, wlast + off + 1), 0) : N_s;
@@ -640,9 +649,9 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   }
 }
 
-template <typename T, int D, int QB, int CS, int AL, int BS>
+template <typename T, int D, int QB, int CS, int AL, int BS, int GQ = 0>
 hipError_t launch_k(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<T, D, QB, CS, AL, BS>), dim3(p.wg_per_xcd * 8), dim3(kWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, QB, CS, AL, BS, GQ>), dim3(p.wg_per_xcd * 8), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -666,6 +675,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     }
     return launch_k<T, D, 1, 2, 2, 0>(p, stream);
   }
+  if (p.gq) return p.alibi ? launch_k<T, D, 1, 1, 1, 0, 1>(p, stream) : launch_k<T, D, 1, 1, 0, 0, 1>(p, stream);
   return p.alibi ? launch_k<T, D, 1, 1, 1, 0>(p, stream) : launch_k<T, D, 1, 1, 0, 0>(p, stream);
 }
 
@@ -676,7 +686,8 @@ hipError_t launch_dtype(int D, const FwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int fwd_block_m(int D, bool causal, bool block_sparse, bool wide) {
+int fwd_block_m(int D, bool causal, bool block_sparse, bool wide, bool gq) {
+  if (gq) return FwdShape<64, 1, 1>::BM;
   if (D == 64) return (wide && !causal && !block_sparse) ? FwdShape<64, 2>::BM : FwdShape<64, 1>::BM;
   return FwdShape<128, 1>::BM;
 }

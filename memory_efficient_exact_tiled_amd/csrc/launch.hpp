@@ -21,6 +21,7 @@ struct FwdParams {
   int B, M, N, Hq, Hkv, group;
   int causal, varlen, alibi;
   int wide;              // dense D=64 without mask: 256-row work-groups (else 128)
+  int gq;                // causal, group % 4 == 0: 32-row work-groups of 4 query heads (one per wave)
   float scale_log2;      // scale * log2(e)
   int n_qtiles;          // dense: q tiles per (batch, head); packed: bound on tiles over all segments
   int total_wg;          // logical work-groups
@@ -79,7 +80,7 @@ struct BwdParams {
 
 // Query rows per forward work-group (wide: the 256-row dense D=64 tiles) and
 // the shortest span of keys of a decode split work-group.
-int fwd_block_m(int D, bool causal, bool block_sparse, bool wide);
+int fwd_block_m(int D, bool causal, bool block_sparse, bool wide, bool gq);
 constexpr int kSparseBlock = 64;   // block edge of block-sparse masks
 constexpr int kDecodeChunk = 64;        // shortest span of keys of a split work-group
 constexpr int kDecodeMaxSplit = 1024;   // most split work-groups (the workspace holds that many + B rows)

@@ -229,6 +229,39 @@ def test_gqa_equals_repeated_kv_bitwise(mea):
         assert np.array_equal(host_bits(o1), host_bits(o2)), causal
 
 
+@pytest.mark.parametrize("D,dt,alibi,Hq,Hkv,packed", [
+    (64, "bf16", False, 8, 2, False), (128, "fp16", True, 8, 2, False), (64, "fp16", True, 16, 2, True),
+    (128, "bf16", True, 32, 8, True), (128, "bf16", False, 4, 1, False)])
+def test_grouped_query_workgroups_bitwise(mea, D, dt, alibi, Hq, Hkv, packed):
+    """Causal launches whose KV heads serve a multiple of 4 query heads run
+    32-row work-groups of 4 query heads (one per wave); with K/V repeated per
+    query head they run the per-head 128-row work-groups. Every row goes
+    through the same arithmetic either way: output and lse bitwise equal, and
+    within the oracle's bar. Ragged sizes, M < N (bottom-right), packed
+    segments of 0..300 tokens."""
+    name = f"gq D={D} {dt} alibi={alibi} Hq={Hq} Hkv={Hkv} packed={packed}"
+    say(f"case {name}")
+    slopes = inp.alibi_slopes(Hq) if alibi else None
+    if packed:
+        c = inp.varlen_case(90, [300, 0, 37, 129, 1, 64, 255], Hq, Hkv, D, dt)
+        st = c["seqstart"]
+    else:
+        c = inp.dense_case(91, 2, 301, 333, Hq, Hkv, D, dt)
+        st = None
+    rep = dict(c, k=np.repeat(c["k"], Hq // Hkv, axis=2), v=np.repeat(c["v"], Hq // Hkv, axis=2))
+    o1, l1, scale = _run(mea, c, dt, causal=True, slopes=slopes, st=st, with_lse=True)
+    o2, l2, _ = _run(mea, rep, dt, causal=True, slopes=slopes, st=st, with_lse=True)
+    assert np.array_equal(host_bits(o1), host_bits(o2))
+    assert torch.equal(l1, l2)
+    want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, scale, causal=True, seqstart_q=st, alibi_slopes=slopes)
+    assert report(name, host_f64(o1), want, TOL[dt]) <= TOL[dt]
+    gl = l1.cpu().numpy()
+    wl = wlse[0] if packed else wlse
+    fin = np.isfinite(wl)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.max(np.abs(gl[fin] - wl[fin]), initial=0.0) <= LSE_TOL[dt]
+
+
 def test_first_causal_row_is_v0_bitwise(mea):
     c = inp.dense_case(33, 2, 130, 130, 4, 2, 128, "bf16")
     out, _, _ = _run(mea, c, "bf16", causal=True, slopes=inp.alibi_slopes(4))
