@@ -363,15 +363,51 @@ def _bits_to_f32(bits, dt):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _lazy_max_outcomes(s):
+    """The forward's per-block choice for D=64 without ALiBi, replayed in fp64.
+
+    s: scores in log2 units [heads, rows, keys] (masked keys -inf). Rows go in
+    groups of 32 (one wave's query block), keys in blocks of 64, each row's
+    keys split into two halves of 32 (the two lanes holding a row). Per
+    group and block the kernel takes P with its running max as the offset
+    (outcome "fast") when every row of the group has a running max and every
+    half-row sum of P stays below 2^7; otherwise it runs the full step
+    ("first" while some row has no running max yet, else "full"), which
+    raises the running maxima to the block maxima when any row's block max
+    exceeds its running max by more than 2^8. Returns the outcome counts."""
+    H, M, N = s.shape
+    counts = {"first": 0, "fast": 0, "full": 0}
+    for g0 in range(0, M, 32):
+        blk = s[:, g0:g0 + 32]
+        m = np.full(blk.shape[:2], -np.inf)
+        for j in range((N + 63) // 64):
+            x = blk[..., j * 64:(j + 1) * 64]
+            for hd in range(H):
+                mh = m[hd]
+                if not np.all(np.isfinite(mh)):
+                    kind = "first"
+                else:
+                    p = np.exp2(x[hd] - mh[:, None])
+                    halves = [p[:, :32].sum(-1), p[:, 32:].sum(-1)]
+                    kind = "fast" if all(np.all(h < 128.0) for h in halves) else "full"
+                counts[kind] += 1
+                if kind != "fast":
+                    bm = x[hd].max(-1)
+                    if np.any(bm > mh + 8.0):
+                        m[hd] = np.maximum(mh, bm)
+    return counts
+
+
 @pytest.mark.parametrize("dt,mode", [("bf16", "rising"), ("fp16", "rising"), ("bf16", "wide")])
 def test_causal_running_max_jumps(mea, dt, mode):
     """Causal D=64 rows whose running max often jumps by more than 2^7 in P
     from one key block to the next ("rising": key norms grow along the
     sequence; "wide": scale 1, scores spread over tens of log2 units), next
-    to blocks where it does not. The forward may take P with the old running
-    max as the offset only when no P of the block reaches 2^7; both outcomes
-    occur in these inputs (checked below in fp64) and must agree with the
-    oracle."""
+    to blocks where it does not. The forward takes P with the old running
+    max as the offset only when no half-row sum of P in a wave's 32 rows
+    reaches 2^7; both outcomes occur in these inputs, per wave and block
+    (replayed below in fp64 with the kernel's own rule), and must agree with
+    the oracle.""" 
     say(f"case causal running max jumps {dt} {mode}")
     B, M, H, D = 2, 1000, 4, 64
     c = inp.dense_case(91, B, M, M, H, H, D, dt)
@@ -393,6 +429,9 @@ def test_causal_running_max_jumps(mea, dt, mode):
     jump = bmax[..., 1:] - run[..., :-1]
     live = np.isfinite(bmax[..., 1:]) & np.isfinite(run[..., :-1])
     assert np.any(live & (jump > 7.5)) and np.any(live & (jump < 0.0))
+    counts = _lazy_max_outcomes(s[0])
+    say(f"lazy max outcomes per (wave, block), batch row 0: {counts}")
+    assert counts["fast"] > 0 and counts["full"] > 0
     out, lse, sc = _run(mea, c, dt, causal=True, scale=scale, with_lse=True)
     want, wlse = orc.fwd(c["q"], c["k"], c["v"], dt, sc, causal=True)
     assert report(f"running max jumps {dt} {mode}", host_f64(out), want, TOL[dt]) <= TOL[dt]
@@ -421,9 +460,14 @@ def test_dense_wide_running_max_jumps(mea, dt, mode):
     bmax = np.stack([s[..., j * 64:(j + 1) * 64].max(-1) for j in range((N + 63) // 64)], -1)
     jump = bmax[..., 1:] - np.maximum.accumulate(bmax, -1)[..., :-1]
     assert np.any(jump > 7.5) and np.any(jump < 0.0)
-    out, _, sc = _run(mea, c, dt, scale=scale)
+    counts = _lazy_max_outcomes(s)
+    say(f"lazy max outcomes per (wave, block), batch row 0: {counts}")
+    assert counts["fast"] > 0 and counts["full"] > 0
+    out, lse, sc = _run(mea, c, dt, scale=scale, with_lse=True)
     got = host_f64(out)
+    got_lse = lse.cpu().numpy()
     rows = np.array([0, 1, 31, 32, 63, 64, 255, 256, 511, 512, 767, 768, 998, 999])
     for b in (0, 7):
-        want, _ = orc.fwd_rows(c["q"], c["k"], c["v"], dt, sc, b, rows)
+        want, wlse = orc.fwd_rows(c["q"], c["k"], c["v"], dt, sc, b, rows)
         assert report(f"dense jumps {dt} {mode} b{b}", got[b, rows], want, TOL[dt]) <= TOL[dt]
+        assert np.max(np.abs(got_lse[b][:, rows] - wlse)) <= LSE_TOL[dt], f"lse b{b}"
