@@ -21,7 +21,12 @@ Prints ONE JSON line on stdout. ``value`` is the headline forward throughput
 (algorithmic TFLOP/s of item 1: 4*B*H*M*N*D flops over its average launch
 time, measured with HIP events on the stream the kernel runs on); the other
 items are reported beside it, decode as algorithmic HBM GB/s (K and V bytes
-of every sequence's context plus q and out). Progress goes to stderr.
+of every sequence's context plus q and out). Each item's ``per_item`` entry
+also carries its algorithmic bytes (inputs read once, outputs written once),
+its arithmetic intensity and the fraction of its own roofline: the longer of
+the MFMA time and the HBM time at peak, over the measured time (the
+block-sparse item, at about 143 flop/B, sits below MI355X's ridge point of
+315 flop/B and is HBM-bound). Progress goes to stderr.
 
 The roofline objects of items 1 and 4 also carry ``alone``: the same kernel
 timed over ALONE consecutive launches on its own (its sustained throughput
@@ -482,15 +487,35 @@ def main():
     }
     ctx = x["decode"]["ctx_host"].astype(np.int64)
     dec_bytes = float(ctx.sum() * 8 * 128 * 2 * 2 + 32 * 32 * 128 * 2 * 2)
+    # Algorithmic HBM bytes per item (every input read once, every output
+    # written once), for each item's own roofline: the bound is whichever of
+    # MFMA time and HBM time is longer at peak.
+    dense_bytes = 4.0 * 4 * 4096 * 16 * 64 * 2                   # q, k, v, out
+    bytes_all = {
+        "fwd_noncausal": dense_bytes,
+        "fwd_causal": dense_bytes,
+        "fwd_varlen": float(L.sum()) * (2 * 32 + 2 * 8) * 128 * 2,  # q, out (Hq); k, v (Hkv)
+        "fwd_blocksparse": 4.0 * MS * 16 * 64 * 2,
+        "bwd_noncausal": 8.0 * 4 * 4096 * 16 * 64 * 2 + 4 * 16 * 4096 * 4,   # q k v out dout, dq dk dv; lse
+        "bwd_causal": 8.0 * 4 * 4096 * 16 * 64 * 2 + 4 * 16 * 4096 * 4,
+    }
     tflops = {n: flops_all[n] / (ms[n] * 1e-3) / 1e12 for n in flops_all if n in ms}
     dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9 if "decode" in ms else None
     per_item = {}
     for n in ms:
         if n in tflops:
             log(f"[bench] {n}: {ms[n] * 1e3:.1f} us  {tflops[n]:.1f} TFLOP/s "
-                f"({tflops[n] / PEAK_MFMA_TFLOPS:.1%} of peak)")
+                f"({tflops[n] / PEAK_MFMA_TFLOPS:.1%} of MFMA peak; {flops_all[n] / bytes_all[n]:.0f} flop/B, "
+                f"{max(flops_all[n] / (PEAK_MFMA_TFLOPS * 1e12), bytes_all[n] / (PEAK_HBM_GBS * 1e9)) / (ms[n] * 1e-3):.1%} "
+                f"of its roofline)")
+            t_mfma = flops_all[n] / (PEAK_MFMA_TFLOPS * 1e12)
+            t_hbm = bytes_all[n] / (PEAK_HBM_GBS * 1e9)
             per_item[n] = {"avg_launch_us": round(ms[n] * 1e3, 2), "tflops": round(tflops[n], 2),
-                           "frac_mfma_peak": round(tflops[n] / PEAK_MFMA_TFLOPS, 4)}
+                           "frac_mfma_peak": round(tflops[n] / PEAK_MFMA_TFLOPS, 4),
+                           "algorithmic_bytes": bytes_all[n],
+                           "intensity_flop_per_byte": round(flops_all[n] / bytes_all[n], 1),
+                           "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                           "frac_roofline": round(max(t_mfma, t_hbm) / (ms[n] * 1e-3), 4)}
         else:
             log(f"[bench] decode: {ms[n] * 1e3:.1f} us  {dec_gbs:.1f} GB/s ({dec_gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
             per_item[n] = {"avg_launch_us": round(ms[n] * 1e3, 2), "gbs": round(dec_gbs, 1),
