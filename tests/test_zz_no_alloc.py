@@ -93,3 +93,35 @@ def test_noalloc_binding_and_limit(mea):
     rc = _noalloc(mea, qb, cache, cache, ctx_big, outb, 0.1, None, mea.MEA_BF16)
     assert rc == mea.MEA_ESCRATCH
     assert "scratch" in mea.strerror(rc)
+
+
+def test_noalloc_inside_a_captured_graph(mea):
+    """The callers the entry point is for: a decode step captured in a HIP
+    graph with no workspace allocated. Three replays, with eager work and
+    synchronisations between them, each bitwise equal to mea_decode."""
+    say("case noalloc graph capture")
+    dt, Hq, Hkv, D = "bf16", 16, 4, 128
+    c = inp.decode_case(64, [900, 1, 4096, 0, 513, 77], 4096, Hq, Hkv, D, dt)
+    q, kc, vc = dev(c["q"], dt), dev(c["kcache"], dt), dev(c["vcache"], dt)
+    ctx_d = i32(c["ctx_lens"])
+    want = mea.decode(q, kc, vc, ctx_d)
+    out = torch.empty_like(q)
+    mea.decode_noalloc(q, kc, vc, ctx_d, out)          # first call on this device: resolves the scratch
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mea.decode_noalloc(q, kc, vc, ctx_d, out)      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mea.decode_noalloc(q, kc, vc, ctx_d, out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), rep
