@@ -345,7 +345,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU clock takes tens of milliseconds to settle after start-up (the
+    # headline launch runs 10-15 % slower in its first ~10 ms): 20 warmup
+    # steps are about 50 ms.
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--items", default="fwd_noncausal,fwd_causal,fwd_varlen,decode,fwd_blocksparse,"
