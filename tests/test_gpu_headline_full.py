@@ -13,7 +13,11 @@ the sizes the benchmark times, element by element against the fp64 oracle:
   segment, output and lse;
 * the decode step, B=32, contexts uniform in [1024, 32768], Hq=32, Hkv=8,
   D=128, bf16, S_max=32768, with every sequence's cache filled: every output
-  element (slots past each context hold NaN and must not be read).
+  element (slots past each context hold NaN and must not be read);
+* the backward at the size the benchmark times it (B=4, M=N=4096, H=16, D=64,
+  bf16, without mask and causal): every element of dq, dk and dv of every
+  (batch row, head), each against its own element-wise bar (the magnitudes of
+  its terms, grad_bounds.py).
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -25,6 +29,7 @@ import torch
 import mea_inputs as inp
 import oracle.attention as orc
 from gpu_util import LSE_TOL, TOL, dev, f32, host_f64, i32, report, say
+from grad_bounds import check_grads, grad_terms
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +121,42 @@ def test_decode_every_sequence(mea):
     out = mea.decode(dev(q_bits, dt), kc.view(torch.bfloat16), vc.view(torch.bfloat16), i32(ctx), scale=scale)
     torch.cuda.synchronize()
     assert report("cfg5 all sequences", host_f64(out), want, TOL[dt]) <= TOL[dt]
+
+
+def _bwd_head(args):
+    """Oracle gradients and their bar terms for one (batch row, head)."""
+    q, k, v, do, scale, causal = args
+    want = orc.bwd(q, k, v, do, "bf16", scale, causal=causal)
+    return want, grad_terms(q, k, v, do, "bf16", scale, causal=causal)[1]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_whole_output(mea, causal):
+    B, M, H, D, dt = 4, 4096, 16, 64, "bf16"
+    name = f"bwd_b4_m4096_h16_{'causal' if causal else 'noncausal'}_whole"
+    say(f"case {name}")
+    c = inp.dense_case(31 + causal, B, M, M, H, H, D, dt)
+    do = inp.normal_bits(531, (B, M, H, D), dt, 0)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    qd, kd, vd, dod = (dev(x, dt) for x in (c["q"], c["k"], c["v"], do))
+    lse = torch.empty((B, H, M), dtype=torch.float32, device="cuda")
+    out = mea.fwd(qd, kd, vd, causal=causal, scale=scale, lse=lse)
+    grads = mea.bwd(qd, kd, vd, out, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    got = [host_f64(g) for g in grads]
+    want = [np.empty_like(g) for g in got]
+    terms = [np.empty_like(g) for g in got]
+    jobs = []
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+            jobs.append(((b, h), (c["q"][sl], c["k"][sl], c["v"][sl], do[sl], scale, causal)))
+    # Each job holds a few 4096 x 4096 float64 matrices (about 1.5 GB).
+    with ThreadPoolExecutor(max_workers=min(WORKERS, 8)) as ex:
+        for (b, h), (w, t) in zip((j[0] for j in jobs), ex.map(_bwd_head, (j[1] for j in jobs))):
+            for arr, x in zip(want, w):
+                arr[b, :, h] = x[0, :, 0]
+            for arr, x in zip(terms, t):
+                arr[b, :, h] = x[0, :, 0]
+    say(f"{name}: oracle done for {B * H} (batch row, head) pairs")
+    check_grads(name, got, want, terms, dt, say=say)
