@@ -1,4 +1,7 @@
 """Parity of the block-sparse forward and backward (``mea_fwd_blocksparse``, ``mea_bwd_blocksparse``) with the fp64 oracle, on the GPU."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -117,6 +120,35 @@ def test_band_global_full_size_sampled(mea):
         err = report(f"band_global h{h}", got[0, rows, h:h + 1], want, TOL["bf16"])
         assert err <= TOL["bf16"]
         assert np.max(np.abs(lse[0, h, rows].cpu().numpy() - wlse[0])) <= LSE_TOL["bf16"]
+
+
+def test_band_global_whole_output(mea):
+    """The benchmark's block-sparse item (its own inputs: B=1, M=N=16384, H=16,
+    D=64, bf16, causal, a window of 3 blocks on each side plus one global key
+    block): every output element and every row's lse against the oracle,
+    evaluated 512 query rows at a time."""
+    say("case blocksparse band_global m16384 whole output")
+    B, M, H, D = 1, 16384, 16, 64
+    c = inp.dense_case(12, B, M, M, H, H, D, "bf16")
+    bm = inp.band_global_block_mask(M // 64, M // 64, 3, 1)
+    out, lse, scale = _run(mea, c, "bf16", bm, causal=True)
+    got, got_lse = host_f64(out)[0], lse.cpu().numpy()[0]
+    q, k, v = (orc.decode_bits(c[x][0], "bf16") for x in ("q", "k", "v"))
+    want = np.empty_like(got)
+    wlse = np.empty_like(got_lse, dtype=np.float64)
+
+    def one(r0):
+        rows = np.arange(r0, min(r0 + 512, M))
+        return rows, orc.attend(q, k, v, scale, True, rows=rows, block_mask=bm)
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        for rows, (w, wl) in ex.map(one, range(0, M, 512)):
+            want[rows] = w
+            wlse[:, rows] = wl
+    assert report("band_global all rows", got, want, TOL["bf16"]) <= TOL["bf16"]
+    err = float(np.max(np.abs(got_lse - wlse)))
+    say(f"[band_global all rows lse] max_abs_err={err:.3e} tol={LSE_TOL['bf16']:.2e}")
+    assert err <= LSE_TOL["bf16"]
 
 
 BWD_CASES = [
