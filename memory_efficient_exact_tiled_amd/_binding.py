@@ -130,6 +130,30 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
+# Shape checks of the arrays the kernels index by the problem's sizes: the C
+# ABI takes plain pointers, so an output or side array smaller than the sizes
+# given would be written or read past its end. They run before any device call.
+def _need_like(t, shape, dtype, what):
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError(f"{what} must be {dtype} shaped {tuple(shape)}")
+
+
+def _need_numel(t, n, dtype, what):
+    if t is not None and (t.numel() != n or t.dtype != dtype):
+        raise ValueError(f"{what} must hold {n} values of {dtype}")
+
+
+def _need_seqstart(seqstart_q, seqstart_k):
+    torch = _torch()
+    for s in (seqstart_q, seqstart_k):
+        if s is not None and (s.dtype != torch.int32 or s.dim() != 1):
+            raise TypeError("seqstart arrays must be 1-D int32 device tensors")
+    if seqstart_k is not None and seqstart_k.numel() != seqstart_q.numel():
+        raise ValueError("seqstart_k must have as many entries as seqstart_q")
+    if seqstart_q.numel() < 2:
+        raise ValueError("seqstart_q needs at least two entries (one segment)")
+
+
 def fwd(q, k, v, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alibi_slopes=None,
         scale: float | None = None, out=None, lse=None, stream=None):
     """Exact attention forward (``mea_fwd``).
@@ -141,23 +165,13 @@ def fwd(q, k, v, *, causal: bool = False, seqstart_q=None, seqstart_k=None, alib
     """
     torch = _torch()
     varlen = seqstart_q is not None
-    if varlen:
-        qv = q.reshape(-1, q.shape[-2], q.shape[-1])
-        kv_ = k.reshape(-1, k.shape[-2], k.shape[-1])
-        M, Hq, D = qv.shape
-        N, Hkv, _ = kv_.shape
-        B = seqstart_q.numel() - 1
-        for s in (seqstart_q, seqstart_k):
-            if s is not None and (s.dtype != torch.int32 or not s.is_cuda):
-                raise TypeError("seqstart arrays must be int32 device tensors")
-    else:
-        B, M, Hq, D = q.shape
-        Bk, N, Hkv, Dk = k.shape
-        if Bk != B or Dk != D:
-            raise ValueError("q and k shapes disagree")
+    B, M, N, Hq, Hkv, D = _shapes(q, k, seqstart_q, seqstart_k)
     if v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("k and v must match in shape and dtype, and q, k, v in dtype")
-    _need_cuda(q, k, v, out, lse, alibi_slopes)
+    _need_like(out, q.shape, q.dtype, "out")
+    _need_numel(lse, (1 if varlen else B) * Hq * M, torch.float32, "lse")
+    _need_numel(alibi_slopes, Hq, torch.float32, "alibi_slopes")
+    _need_cuda(q, k, v, out, lse, alibi_slopes, seqstart_q, seqstart_k)
     if out is None:
         out = torch.empty_like(q)
     if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
@@ -190,6 +204,9 @@ def fwd_blocksparse(q, k, v, block_mask, *, causal: bool = False, alibi_slopes=N
         raise ValueError(f"block_mask must be uint8/bool [{-(-M // blk)}, {-(-N // blk)}]")
     if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
         raise TypeError("alibi_slopes must be float32")
+    _need_like(out, q.shape, q.dtype, "out")
+    _need_numel(lse, B * Hq * M, torch.float32, "lse")
+    _need_numel(alibi_slopes, Hq, torch.float32, "alibi_slopes")
     _need_cuda(q, k, v, out, lse, alibi_slopes, block_mask)
     out = torch.empty_like(q) if out is None else out
     if scale is None:
@@ -204,14 +221,18 @@ def fwd_blocksparse(q, k, v, block_mask, *, causal: bool = False, alibi_slopes=N
 def _shapes(q, k, seqstart_q, seqstart_k):
     torch = _torch()
     if seqstart_q is not None:
-        M, Hq, D = q.shape[-3:]
-        N, Hkv, _ = k.shape[-3:]
-        if q.numel() != M * Hq * D or k.numel() != N * Hkv * D:
+        if q.dim() not in (3, 4) or k.dim() not in (3, 4):
             raise ValueError("packed q/k must be [1,T,H,D] or [T,H,D]")
-        for s in (seqstart_q, seqstart_k):
-            if s is not None and (s.dtype != torch.int32 or not s.is_cuda):
-                raise TypeError("seqstart arrays must be int32 device tensors")
+        M, Hq, D = q.shape[-3:]
+        N, Hkv, Dk = k.shape[-3:]
+        if q.numel() != M * Hq * D or k.numel() != N * Hkv * Dk or Dk != D:
+            raise ValueError("packed q/k must be [1,T,H,D] or [T,H,D]")
+        _need_seqstart(seqstart_q, seqstart_k)
         return seqstart_q.numel() - 1, M, N, Hq, Hkv, D
+    if seqstart_k is not None:
+        raise ValueError("seqstart_k needs seqstart_q")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("dense q/k must be [B,M,Hq,D] / [B,N,Hkv,D]")
     B, M, Hq, D = q.shape
     Bk, N, Hkv, Dk = k.shape
     if Bk != B or Dk != D:
@@ -239,7 +260,11 @@ def bwd(q, k, v, out, dout, lse, *, causal: bool = False, seqstart_q=None, seqst
         raise ValueError("lse must be the float32 [B,Hq,M] (packed [Hq,M]) array the forward filled")
     if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
         raise TypeError("alibi_slopes must be float32")
-    _need_cuda(q, k, v, out, dout, lse, dq, dk, dv, alibi_slopes, workspace)
+    _need_numel(alibi_slopes, Hq, torch.float32, "alibi_slopes")
+    _need_like(dq, q.shape, q.dtype, "dq")
+    _need_like(dk, k.shape, q.dtype, "dk")
+    _need_like(dv, v.shape, q.dtype, "dv")
+    _need_cuda(q, k, v, out, dout, lse, dq, dk, dv, alibi_slopes, workspace, seqstart_q, seqstart_k)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -280,6 +305,8 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, alibi_slo
         raise ValueError("q and caches must share a dtype")
     if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
         raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_like(out, q.shape, q.dtype, "out")
+    _need_numel(alibi_slopes, Hq, torch.float32, "alibi_slopes")
     _need_cuda(q, kcache, vcache, ctx_lens, out, alibi_slopes, workspace)
     if out is None:
         out = torch.empty_like(q)
@@ -309,6 +336,7 @@ def decode_noalloc(q, kcache, vcache, ctx_lens, out, *, scale: float | None = No
         raise ValueError("q, caches and out must share a dtype; out is shaped like q")
     if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
         raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_numel(alibi_slopes, Hq, torch.float32, "alibi_slopes")
     _need_cuda(q, kcache, vcache, ctx_lens, out, alibi_slopes)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -331,6 +359,9 @@ def fwd_kvcache(q, kcache, vcache, ctx_lens, *, causal: bool = True, alibi_slope
         raise ValueError("q and caches must share a dtype")
     if ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B:
         raise TypeError("ctx_lens must be an int32 device tensor of B entries")
+    _need_like(out, q.shape, q.dtype, "out")
+    _need_numel(lse, B * Hq * M, torch.float32, "lse")
+    _need_numel(alibi_slopes, Hq, torch.float32, "alibi_slopes")
     _need_cuda(q, kcache, vcache, ctx_lens, out, lse, alibi_slopes)
     if out is None:
         out = torch.empty_like(q)
