@@ -127,7 +127,12 @@ decode_split_kernel(const DecParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // The wave index is made visibly wave-uniform: the K/V buffer resources
+  // depend on it (through the KV head), and a resource the compiler takes
+  // for divergent turns every load into a loop over lanes (readfirstlane,
+  // compare, exec mask) whose pending loads its wait counting then
+  // overestimates, so each step waited for the loads of the next.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // [B + 1] prefix sums of ctx, then L: from the plan kernel, or (small
   // batches) computed here by wave 0 into LDS, work-group (0, 0) also
   // storing it for the combine.
@@ -312,21 +317,26 @@ decode_split_kernel(const DecParams p) {
     __asm__ volatile("" ::: "memory");
   };
 
+  // The next stages' loads are issued unconditionally: a step at or past w1
+  // gets an empty buffer resource, so its loads return zeros without
+  // touching memory. A conditional prefetch leaves the compiler unsure
+  // whether those loads are in flight, and its wait counts then assume they
+  // are not: each step waited for the loads of the next one as well.
   if constexpr (STAGES == 3) {
     Stage s0, s1, s2;
     int key0 = w0;
     load(s0, key0);
-    if (key0 + KSTEP < w1) load(s1, key0 + KSTEP);
+    load(s1, key0 + KSTEP);
     while (true) {
-      if (key0 + 2 * KSTEP < w1) load(s2, key0 + 2 * KSTEP);
+      load(s2, key0 + 2 * KSTEP);
       compute(s0, key0);
       key0 += KSTEP;
       if (key0 >= w1) break;
-      if (key0 + 2 * KSTEP < w1) load(s0, key0 + 2 * KSTEP);
+      load(s0, key0 + 2 * KSTEP);
       compute(s1, key0);
       key0 += KSTEP;
       if (key0 >= w1) break;
-      if (key0 + 2 * KSTEP < w1) load(s1, key0 + 2 * KSTEP);
+      load(s1, key0 + 2 * KSTEP);
       compute(s2, key0);
       key0 += KSTEP;
       if (key0 >= w1) break;
@@ -336,11 +346,11 @@ decode_split_kernel(const DecParams p) {
     int key0 = w0;
     load(sa, key0);
     while (true) {
-      if (key0 + KSTEP < w1) load(sb, key0 + KSTEP);
+      load(sb, key0 + KSTEP);
       compute(sa, key0);
       key0 += KSTEP;
       if (key0 >= w1) break;
-      if (key0 + KSTEP < w1) load(sa, key0 + KSTEP);
+      load(sa, key0 + KSTEP);
       compute(sb, key0);
       key0 += KSTEP;
       if (key0 >= w1) break;

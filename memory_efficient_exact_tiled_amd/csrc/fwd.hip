@@ -131,8 +131,10 @@ __attribute__((amdgpu_waves_per_eu(FwdShape<D, QB_>::WPE, FwdShape<D, QB_>::WPE)
   const int lane = tid & 63;
   // Under a causal mask the wave index is made visibly wave-uniform, so the
   // per-wave mask decisions compile to scalar branches (measured faster
-  // there; the dense launch schedules better without it).
-  const int wave = CS == 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
+  // there; the dense D=64 launch schedules better without it). At D=128 it
+  // also keeps the LDS DMA copies, whose LDS address (M0) and count depend
+  // on the wave, out of divergent branches and lane loops.
+  const int wave = (CS == 1 || D == 128) ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
